@@ -1,0 +1,160 @@
+/*
+ * qsa.h -- C ABI of libqsa.so, the QSA token indexer's hot path on one AMD
+ * Instinct MI355X (gfx950): pool -> score -> select/mask.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SEL]   pegainfer pull request 1178, "select QSA indexer blocks and their tail"
+ *   [SCORE] pegainfer pull request 1160, "score QSA token-indexer blocks in native CUDA"
+ *   [QSA]   metrale model layers, layers/qsa.rs (source view)
+ *
+ * Geometry is compiled in: 4 query heads, head dim 128, 4-token blocks, at most
+ * 512 kept blocks per row ([SCORE] "Frozen semantics"; [SEL] "Exact semantics").
+ * rotary_dim, rope_theta, rms_eps and budget are run-time arguments.
+ *
+ * Conventions shared by every call:
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are
+ *     row-major, in device memory, owned by the caller.
+ *   - The library allocates, frees, synchronises and reads back nothing.
+ *     All work is enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *     Calls are thread-safe and keep no state between calls.
+ *   - Host-side refusals return a negative QSA_ERR_* code before any launch;
+ *     nothing is written then.  An empty launch (zero rows / tokens / blocks)
+ *     returns QSA_OK and enqueues nothing.
+ *   - Device-side refusals never trap: kernels OR bits into the caller-owned,
+ *     caller-zeroed int32 *dev_status (QSA_STATUS_*) and write the documented
+ *     fallback for the offending row.
+ *   - Supported key caches hold at most QSA_MAX_TOKENS tokens.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+#define QSA_HEADS 4
+#define QSA_HEAD_DIM 128
+#define QSA_RATIO 4
+#define QSA_MAX_KEEP_BLOCKS 512
+/* 65536 blocks plus a 3-token tail: the longest row whose visible blocks the
+ * selector holds on chip. */
+#define QSA_MAX_TOKENS 262147
+
+/* Return codes. */
+#define QSA_OK 0
+#define QSA_ERR_NULL (-1)     /* a required pointer is NULL while its extent is > 0 */
+#define QSA_ERR_EXTENT (-2)   /* negative extent, or a block range past tokens/4 */
+#define QSA_ERR_BUDGET (-3)   /* budget not a positive multiple of 4, or budget/4 > 512 */
+#define QSA_ERR_STRIDE (-4)   /* a row stride narrower than its row */
+#define QSA_ERR_CAPACITY (-5) /* an output buffer too short, or tokens > QSA_MAX_TOKENS */
+#define QSA_ERR_PARAM (-6)    /* rotary_dim, rope_theta or rms_eps out of range */
+#define QSA_ERR_LAUNCH (-7)   /* the HIP runtime refused the launch */
+
+/* Bits OR-ed into *dev_status by the kernels. */
+#define QSA_STATUS_BAD_POSITION 1   /* pos[r] outside [0, tokens) */
+#define QSA_STATUS_NONFINITE_SCORE 2 /* a NaN or +-Inf among a row's visible block scores */
+
+/*
+ * qsa_pool_keys -- pooled key of every 4-token block in
+ * [first_block, first_block + n_blocks).
+ *
+ * [SCORE] summary: the block's four raw keys are averaged in float32 and cast
+ * to bf16, then (1 + w) RMSNorm with k_norm_w and partial RoPE at the block's
+ * first token 4b.  [QSA] pool_new_blocks: only newly completed blocks need
+ * pooling, hence the block range.
+ *
+ *   raw_keys    [tokens, key_stride] bf16; the key is the first 128 columns of
+ *               each row.  key_stride >= 128 (elements).
+ *   k_norm_w    [128] bf16 norm weight (the scale is 1 + w).
+ *   rotary_dim  even, 0..128: channels [0, rotary_dim) rotate as pairs
+ *               (i, i + rotary_dim/2) at frequency theta^(-2i/rotary_dim);
+ *               the rest pass through.
+ *   rope_theta  > 0 and finite.   rms_eps  >= 0 and finite.
+ *   pooled      [tokens/4, 128] bf16; rows [first_block, first_block+n_blocks)
+ *               are written, all others untouched.
+ * Refusals: NULL pointers (QSA_ERR_NULL); negative extents or
+ * first_block + n_blocks > tokens/4 (QSA_ERR_EXTENT); key_stride < 128
+ * (QSA_ERR_STRIDE); bad rotary_dim / theta / eps (QSA_ERR_PARAM).
+ */
+int qsa_pool_keys(const uint16_t* raw_keys, int64_t key_stride, int64_t tokens,
+                  const uint16_t* k_norm_w, int32_t rotary_dim, float rope_theta,
+                  float rms_eps, int64_t first_block, int64_t n_blocks,
+                  uint16_t* pooled, void* stream);
+
+/*
+ * qsa_score_rows -- block scores of query rows against the pooled keys.
+ *
+ * [SCORE] summary: each of the row's 4 query heads is (1 + w) RMSNorm-ed with
+ * q_norm_w and roped at the row's own position p; the score of block b is
+ * sum_h relu(q_h . k_b) / sqrt(128), relu per head before the head sum, f32.
+ * relu keeps NaN, so a poisoned key scores NaN ([SCORE] review).  Row r sees
+ * blocks b < (pos[r] + 1) / 4 ([SEL] "Exact semantics").
+ *
+ *   q           [rows, q_stride] bf16; heads h at columns [128h, 128h + 128).
+ *               q_stride >= 512 (elements).
+ *   pos         [rows] int32 row positions, token 0 first visible.
+ *   q_norm_w    [128] bf16.
+ *   pooled      [tokens/4, 128] bf16 from qsa_pool_keys.
+ *   scores      f32, row stride score_cols >= tokens/4, scores_len elements
+ *               (spare capacity allowed).  Exactly scores[r*score_cols + b] for
+ *               b < (pos[r]+1)/4 is written; every other element is untouched.
+ *   dev_status  int32 flag word; a row with pos outside [0, tokens) sets
+ *               QSA_STATUS_BAD_POSITION and writes nothing.
+ * Refusals: QSA_ERR_NULL, QSA_ERR_EXTENT (negative rows/tokens),
+ * QSA_ERR_STRIDE (q_stride < 512, score_cols < tokens/4), QSA_ERR_CAPACITY
+ * (scores_len < rows*score_cols, tokens > QSA_MAX_TOKENS), QSA_ERR_PARAM.
+ */
+int qsa_score_rows(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                   const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
+                   float rms_eps, const uint16_t* pooled, int64_t tokens, float* scores,
+                   int64_t score_cols, int64_t scores_len, int32_t* dev_status,
+                   void* stream);
+
+/*
+ * qsa_select_mask -- exact per-row top-(budget/4) block select and the u8
+ * token visibility mask.
+ *
+ * [SEL] "Exact semantics": for a row at position p, blocks n = (p+1)/4, tail
+ * = (p+1)%4 tokens at 4n..p, keep = min(budget/4, n).  The keep first blocks
+ * under the order (score descending, block index ascending; -0.0 ties +0.0)
+ * are kept.  mask[r*tokens + t] = 1 for the 4 tokens of every kept block and
+ * for the tail, 0 for every other t in [0, tokens).
+ *
+ *   scores      f32, row stride score_cols >= tokens/4, scores_len elements;
+ *               only each row's first (p+1)/4 entries are read.
+ *   pos         [rows] int32.
+ *   budget      positive multiple of 4, budget/4 <= 512.
+ *   mask        [rows, tokens] u8, every byte written.
+ *   dev_status  a row with pos outside [0, tokens) sets QSA_STATUS_BAD_POSITION;
+ *               a row with a non-finite score among its first (p+1)/4 sets
+ *               QSA_STATUS_NONFINITE_SCORE.  Such rows are written all zero.
+ * Refusals: QSA_ERR_NULL, QSA_ERR_EXTENT, QSA_ERR_BUDGET, QSA_ERR_STRIDE
+ * (score_cols < tokens/4), QSA_ERR_CAPACITY (scores_len < rows*score_cols,
+ * tokens > QSA_MAX_TOKENS).
+ */
+int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
+                    const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                    uint8_t* mask, int32_t* dev_status, void* stream);
+
+/*
+ * qsa_rope_inv_freq -- host only: the rotary frequencies the kernels use,
+ * out[i] = (float)(theta^(-2i/rotary_dim)) evaluated in double, i < rotary_dim/2.
+ * Returns QSA_ERR_NULL / QSA_ERR_PARAM on bad arguments.
+ */
+int qsa_rope_inv_freq(int32_t rotary_dim, float rope_theta, float* out);
+
+/* Static description of a return code.  Never NULL. */
+const char* qsa_strerror(int code);
+
+/* QSA_ABI_VERSION of the loaded library. */
+int qsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,139 @@
+"""QSA token indexer hot path on AMD Instinct MI355X (gfx950).
+
+Thin torch-facing binding of libqsa.so (C ABI: include/qsa.h).  Each function
+has the name of the C entry point it marshals to; torch tensors supply device
+memory, torch's current HIP stream is used unless one is given.  All
+computation runs in the library's HIP kernels; there is no CPU path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,  # noqa: F401
+                   STATUS_BAD_POSITION, STATUS_NONFINITE_SCORE, QsaError, abi_version, load,
+                   strerror)
+
+__all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_select_mask", "qsa_rope_inv_freq",
+           "check_status", "load", "abi_version", "strerror", "QsaError"]
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be on the GPU")
+    _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _rows_2d(t: torch.Tensor, name: str, min_cols: int) -> int:
+    """Row stride (elements) of a 2-D tensor with unit column stride."""
+    _need(t.dim() == 2, f"{name} must be 2-D")
+    _need(t.stride(1) == 1 or t.shape[1] == 1, f"{name} must have unit column stride")
+    _need(t.shape[1] >= min_cols, f"{name} needs at least {min_cols} columns")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise QsaError(code, what)
+
+
+def qsa_pool_keys(raw_keys: torch.Tensor, k_norm_w: torch.Tensor, rotary_dim: int,
+                  rope_theta: float, rms_eps: float, pooled: torch.Tensor,
+                  first_block: int = 0, n_blocks: int | None = None, stream=None) -> None:
+    """Pool blocks [first_block, first_block + n_blocks) of raw_keys
+    [tokens, >=128] (bf16, unit column stride) into pooled [tokens/4, 128]."""
+    _dev(raw_keys, "raw_keys", _BF16_LIKE)
+    _dev(k_norm_w, "k_norm_w", _BF16_LIKE)
+    _dev(pooled, "pooled", _BF16_LIKE)
+    key_stride = _rows_2d(raw_keys, "raw_keys", HEAD_DIM)
+    tokens = raw_keys.shape[0]
+    _need(k_norm_w.numel() == HEAD_DIM and k_norm_w.is_contiguous(), "k_norm_w must hold 128 values")
+    _need(pooled.is_contiguous() and pooled.dim() == 2 and pooled.shape[1] == HEAD_DIM
+          and pooled.shape[0] >= tokens // RATIO, "pooled must be contiguous [tokens/4, 128]")
+    if n_blocks is None:
+        n_blocks = tokens // RATIO - first_block
+    lib = load()
+    _check(lib.qsa_pool_keys(_ptr(raw_keys), key_stride, tokens, _ptr(k_norm_w), rotary_dim,
+                             rope_theta, rms_eps, first_block, n_blocks, _ptr(pooled),
+                             _stream_ptr(stream)), "qsa_pool_keys")
+
+
+def qsa_score_rows(q: torch.Tensor, pos: torch.Tensor, q_norm_w: torch.Tensor, rotary_dim: int,
+                   rope_theta: float, rms_eps: float, pooled: torch.Tensor, tokens: int,
+                   scores: torch.Tensor, score_cols: int, dev_status: torch.Tensor,
+                   stream=None) -> None:
+    """Scores of query rows q [rows, >=512] (4 heads x 128, bf16) at positions
+    pos (int32 [rows]) against pooled keys; writes scores[r*score_cols + b]
+    for b < (pos[r]+1)/4 into the flat f32 buffer `scores`."""
+    _dev(q, "q", _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(q_norm_w, "q_norm_w", _BF16_LIKE)
+    _dev(pooled, "pooled", _BF16_LIKE)
+    _dev(scores, "scores", (torch.float32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    q_stride = _rows_2d(q, "q", HEADS * HEAD_DIM)
+    rows = q.shape[0]
+    _need(pos.is_contiguous() and pos.numel() == rows, "pos must be contiguous [rows]")
+    _need(q_norm_w.numel() == HEAD_DIM and q_norm_w.is_contiguous(), "q_norm_w must hold 128 values")
+    _need(pooled.is_contiguous() and pooled.numel() >= (tokens // RATIO) * HEAD_DIM,
+          "pooled must be contiguous and cover tokens/4 blocks")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    lib = load()
+    _check(lib.qsa_score_rows(_ptr(q), q_stride, _ptr(pos), rows, _ptr(q_norm_w), rotary_dim,
+                              rope_theta, rms_eps, _ptr(pooled), tokens, _ptr(scores),
+                              score_cols, scores.numel(), _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_score_rows")
+
+
+def qsa_select_mask(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, tokens: int,
+                    budget: int, mask: torch.Tensor, dev_status: torch.Tensor,
+                    stream=None) -> None:
+    """Top-(budget/4) block select of each row and its u8 mask [rows, tokens]."""
+    _dev(scores, "scores", (torch.float32,))
+    _dev(pos, "pos", (torch.int32,))
+    _dev(mask, "mask", (torch.uint8,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous(), "pos must be contiguous")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    _need(mask.is_contiguous() and mask.numel() >= rows * tokens, "mask must be contiguous [rows, tokens]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    lib = load()
+    _check(lib.qsa_select_mask(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
+                               budget, _ptr(mask), _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_select_mask")
+
+
+def qsa_rope_inv_freq(rotary_dim: int, rope_theta: float) -> list:
+    """The library's rotary frequencies (host computation), as Python floats."""
+    lib = load()
+    buf = (ctypes.c_float * max(1, rotary_dim // 2))()
+    _check(lib.qsa_rope_inv_freq(rotary_dim, rope_theta, buf), "qsa_rope_inv_freq")
+    return [buf[i] for i in range(rotary_dim // 2)]
+
+
+def check_status(dev_status: torch.Tensor) -> int:
+    """Synchronise and return the status word (QSA_STATUS_* bits)."""
+    torch.cuda.synchronize(dev_status.device)
+    return int(dev_status.view(-1)[0].item())

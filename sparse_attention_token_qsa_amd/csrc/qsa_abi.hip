@@ -1,0 +1,128 @@
+// C ABI of libqsa.so: argument refusals, rotary table, launches.
+// Contract and citations: include/qsa.h.  Every refusal returns before any
+// HIP call, so this layer is exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/qsa.h"
+#include "qsa_launch.h"
+
+namespace {
+
+bool mul_overflows(int64_t a, int64_t b, int64_t* out) {
+  return __builtin_mul_overflow(a, b, out);
+}
+
+int check_rope(int32_t rotary_dim, float theta, float eps) {
+  if (rotary_dim < 0 || rotary_dim > QSA_HEAD_DIM || (rotary_dim & 1)) return QSA_ERR_PARAM;
+  if (!(theta > 0.0f) || !isfinite(theta)) return QSA_ERR_PARAM;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return QSA_ERR_PARAM;
+  return QSA_OK;
+}
+
+void fill_inv_freq(int32_t rotary_dim, float theta, float* out) {
+  const int half = rotary_dim / 2;
+  for (int i = 0; i < half; ++i)
+    out[i] = static_cast<float>(pow(static_cast<double>(theta), -(2.0 * i) / static_cast<double>(rotary_dim)));
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char* qsa_strerror(int code) {
+  switch (code) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL: return "qsa: a required pointer is NULL";
+    case QSA_ERR_EXTENT: return "qsa: negative extent or block range past tokens/4";
+    case QSA_ERR_BUDGET: return "qsa: budget must be a positive multiple of 4 with budget/4 <= 512";
+    case QSA_ERR_STRIDE: return "qsa: a row stride is narrower than its row";
+    case QSA_ERR_CAPACITY: return "qsa: output buffer too short or tokens above the supported maximum";
+    case QSA_ERR_PARAM: return "qsa: rotary_dim, rope_theta or rms_eps out of range";
+    case QSA_ERR_LAUNCH: return "qsa: the HIP runtime refused the launch";
+    default: return "qsa: unknown error code";
+  }
+}
+
+int qsa_rope_inv_freq(int32_t rotary_dim, float rope_theta, float* out) {
+  const int rc = check_rope(rotary_dim, rope_theta, 0.0f);
+  if (rc != QSA_OK) return rc;
+  if (rotary_dim > 0 && out == nullptr) return QSA_ERR_NULL;
+  fill_inv_freq(rotary_dim, rope_theta, out);
+  return QSA_OK;
+}
+
+int qsa_pool_keys(const uint16_t* raw_keys, int64_t key_stride, int64_t tokens,
+                  const uint16_t* k_norm_w, int32_t rotary_dim, float rope_theta,
+                  float rms_eps, int64_t first_block, int64_t n_blocks, uint16_t* pooled,
+                  void* stream) {
+  if (tokens < 0 || first_block < 0 || n_blocks < 0) return QSA_ERR_EXTENT;
+  if (first_block > tokens / QSA_RATIO || n_blocks > tokens / QSA_RATIO - first_block)
+    return QSA_ERR_EXTENT;
+  if (key_stride < QSA_HEAD_DIM) return QSA_ERR_STRIDE;
+  const int rc = check_rope(rotary_dim, rope_theta, rms_eps);
+  if (rc != QSA_OK) return rc;
+  if (n_blocks == 0) return QSA_OK;
+  if (raw_keys == nullptr || k_norm_w == nullptr || pooled == nullptr) return QSA_ERR_NULL;
+  int64_t span;
+  if (mul_overflows(tokens, key_stride, &span)) return QSA_ERR_CAPACITY;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_pool(raw_keys, key_stride, k_norm_w, rp, first_block,
+                                        n_blocks, pooled, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_score_rows(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                   const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
+                   float rms_eps, const uint16_t* pooled, int64_t tokens, float* scores,
+                   int64_t score_cols, int64_t scores_len, int32_t* dev_status, void* stream) {
+  if (rows < 0 || tokens < 0 || score_cols < 0 || scores_len < 0) return QSA_ERR_EXTENT;
+  if (q_stride < QSA_HEADS * QSA_HEAD_DIM) return QSA_ERR_STRIDE;
+  if (score_cols < tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  const int rc = check_rope(rotary_dim, rope_theta, rms_eps);
+  if (rc != QSA_OK) return rc;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0 || tokens == 0) return QSA_OK;
+  if (q == nullptr || pos == nullptr || q_norm_w == nullptr || dev_status == nullptr)
+    return QSA_ERR_NULL;
+  if (tokens >= QSA_RATIO && (pooled == nullptr || scores == nullptr)) return QSA_ERR_NULL;
+  if (mul_overflows(rows, q_stride, &need)) return QSA_ERR_CAPACITY;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_score(q, q_stride, pos, rows, q_norm_w, rp, pooled, tokens,
+                                         scores, score_cols, dev_status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
+                    const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                    uint8_t* mask, int32_t* dev_status, void* stream) {
+  if (rows < 0 || tokens < 0 || score_cols < 0 || scores_len < 0) return QSA_ERR_EXTENT;
+  if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
+    return QSA_ERR_BUDGET;
+  if (score_cols < tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
+  if (mul_overflows(rows, tokens, &need)) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;  // one workgroup per row
+  if (rows == 0 || tokens == 0) return QSA_OK;
+  if (pos == nullptr || mask == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
+  if (tokens >= QSA_RATIO && scores == nullptr) return QSA_ERR_NULL;
+  return launch_status(qsa::launch_select(scores, score_cols, pos, rows, tokens,
+                                          static_cast<int>(budget / QSA_RATIO), mask,
+                                          dev_status, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device-side helpers shared by the pool, score and select kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kHeads = 4;
+constexpr int kHeadDim = 128;
+constexpr int kRatio = 4;
+constexpr int kMaxKeep = 512;
+constexpr int kMaxHalfRotary = 64;
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bit pattern, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Round a float to the nearest bf16 value, returned as float.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// Order-preserving map of a finite float to u32: a larger score gives a
+// larger key; -0.0 is folded onto +0.0 so the two zeros tie.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bool is_finite_bits(float s) {
+  return (__float_as_uint(s) & 0x7F800000u) != 0x7F800000u;
+}
+
+// Rotary angle of position `p` at frequency `f`: one f32 product, then cos
+// and sin evaluated in double on that f32 angle and rounded to f32 and bf16.
+__device__ __forceinline__ void rope_cos_sin(int64_t p, float f, float& c, float& s) {
+#pragma clang fp contract(off)
+  const float angle = static_cast<float>(p) * f;
+  double sd, cd;
+  sincos(static_cast<double>(angle), &sd, &cd);
+  c = round_bf16(static_cast<float>(cd));
+  s = round_bf16(static_cast<float>(sd));
+}
+
+// Inverse RMS of a 128-channel vector from its sum of squares (double):
+// 1 / sqrt(ss / 128 + eps).
+__device__ __forceinline__ double inv_rms(double ss, float eps) {
+#pragma clang fp contract(off)
+  const double ms = ss / 128.0;
+  return 1.0 / sqrt(ms + static_cast<double>(eps));
+}
+
+// (1 + w) RMSNorm output of one bf16 channel value x, rounded to bf16.
+__device__ __forceinline__ float norm_channel(float x, double r, float w) {
+#pragma clang fp contract(off)
+  const double y = (static_cast<double>(x) * r) * (1.0 + static_cast<double>(w));
+  return round_bf16(static_cast<float>(y));
+}
+
+// Rotated value of channel x against its partner xp with bf16 rounding after
+// every op: first half  o = rb(rb(x c) - rb(xp s)),
+//           second half o = rb(rb(x c) + rb(xp s)).
+__device__ __forceinline__ float rope_channel(float x, float xp, float c, float s, bool first_half) {
+#pragma clang fp contract(off)
+  const float a = round_bf16(x * c);
+  const float b = round_bf16(xp * s);
+  return round_bf16(first_half ? (a - b) : (a + b));
+}
+
+}  // namespace qsa

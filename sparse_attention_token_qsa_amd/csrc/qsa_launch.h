@@ -1,0 +1,29 @@
+// Internal launch interface between the C ABI layer and the kernels.
+// Arguments reach here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct RopeParams {
+  int rotary_dim;
+  float eps;
+  float inv_freq[64];
+};
+
+hipError_t launch_pool(const uint16_t* raw, int64_t key_stride, const uint16_t* w,
+                       const RopeParams& rp, int64_t first_block, int64_t n_blocks,
+                       uint16_t* pooled, hipStream_t stream);
+
+hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                        const uint16_t* w, const RopeParams& rp, const uint16_t* pooled,
+                        int64_t tokens, float* scores, int64_t score_cols, int32_t* status,
+                        hipStream_t stream);
+
+hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t* pos,
+                         int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
+                         int32_t* status, hipStream_t stream);
+
+}  // namespace qsa

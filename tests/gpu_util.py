@@ -1,0 +1,81 @@
+"""Helpers for the GPU tests: move seeded inputs to the device, run the three
+C-ABI calls through the binding, read results back.  No method arithmetic."""
+
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import sparse_attention_token_qsa_amd as qsa
+import synth
+
+DEV = "cuda:0"
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def u16_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def u16_host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def i32_dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def f32_dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+@functools.lru_cache(maxsize=8)
+def workload(wid: int):
+    return synth.make_workload(wid)
+
+
+def status_word() -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=DEV)
+
+
+def gpu_pool(w, first_block=0, n_blocks=None, raw_dev=None, key_stride_view=None):
+    T = w["tokens"]
+    raw = u16_dev(w["raw_keys"]) if raw_dev is None else raw_dev
+    if key_stride_view is not None:
+        raw = key_stride_view
+    pooled = torch.full((T // 4, 128), 0x5A5A, dtype=torch.int16, device=DEV)
+    qsa.qsa_pool_keys(raw, u16_dev(w["k_norm_w"]), w["rotary_dim"], w["theta"], w["eps"], pooled,
+                      first_block=first_block, n_blocks=n_blocks)
+    torch.cuda.synchronize()
+    return pooled
+
+
+def gpu_scores(w, pooled_dev, pos=None, q=None, score_cols=None, sentinel=np.float32(-7.25)):
+    """Scores [rows, score_cols] (read back), prefilled with `sentinel`, and status."""
+    T = w["tokens"]
+    pos = w["pos"] if pos is None else pos
+    q = w["queries"] if q is None else q
+    rows = len(pos)
+    cols = T // 4 if score_cols is None else score_cols
+    scores = torch.full((rows * max(cols, 1),), float(sentinel), dtype=torch.float32, device=DEV)
+    st = status_word()
+    qsa.qsa_score_rows(u16_dev(q.reshape(rows, 512)), i32_dev(pos), u16_dev(w["q_norm_w"]),
+                       w["rotary_dim"], w["theta"], w["eps"], pooled_dev, T, scores, cols, st)
+    s = qsa.check_status(st)
+    return scores.cpu().numpy().reshape(rows, max(cols, 1)), s
+
+
+def gpu_select(scores: np.ndarray, cols: int, pos, tokens: int, budget: int):
+    rows = len(pos)
+    mask = torch.full((rows, tokens), 0xAB, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    qsa.qsa_select_mask(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, mask, st)
+    s = qsa.check_status(st)
+    return mask.cpu().numpy(), s

@@ -1,0 +1,150 @@
+"""libqsa.so on the host: it loads, exports every symbol include/qsa.h
+declares, and refuses bad arguments before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from sparse_attention_token_qsa_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+# Fake, never dereferenced device addresses: every call below is refused (or
+# is an empty launch) before the library touches HIP.
+P = 0x1000
+OK, NULL, EXTENT, BUDGET, STRIDE, CAP, PARAM = 0, -1, -2, -3, -4, -5, -6
+
+
+# These calls pass fake addresses that a launch would dereference; they are
+# meant for a host with no GPU (on a GPU host a validation bug would fault).
+pytestmark = pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                                reason="fake-pointer refusal checks run on a host without a GPU")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.qsa_abi_version() == 1
+    for code in range(-7, 1):
+        assert lib.qsa_strerror(code)
+    assert b"unknown" in lib.qsa_strerror(-99)
+
+
+@pytest.mark.parametrize("rd,theta", [(64, 1e4), (64, 1e7), (128, 5e5), (2, 1e4), (36, 123.5)])
+def test_host_rope_frequencies_match_the_oracle_bitwise(lib, rd, theta):
+    buf = (ctypes.c_float * (rd // 2))()
+    assert lib.qsa_rope_inv_freq(rd, theta, buf) == OK
+    ours = np.frombuffer(buf, dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), O.rope_inv_freq(rd, theta).view(np.uint32))
+
+
+def test_rope_frequency_refusals(lib):
+    buf = (ctypes.c_float * 64)()
+    assert lib.qsa_rope_inv_freq(63, 1e4, buf) == PARAM
+    assert lib.qsa_rope_inv_freq(130, 1e4, buf) == PARAM
+    assert lib.qsa_rope_inv_freq(64, 0.0, buf) == PARAM
+    assert lib.qsa_rope_inv_freq(64, float("inf"), buf) == PARAM
+    assert lib.qsa_rope_inv_freq(64, 1e4, None) == NULL
+    assert lib.qsa_rope_inv_freq(0, 1e4, None) == OK
+
+
+def pool(lib, **kw):
+    a = dict(raw=P, key_stride=128, tokens=64, w=P, rd=64, theta=1e4, eps=1e-6,
+             first_block=0, n_blocks=16, pooled=P)
+    a.update(kw)
+    return lib.qsa_pool_keys(a["raw"], a["key_stride"], a["tokens"], a["w"], a["rd"], a["theta"],
+                             a["eps"], a["first_block"], a["n_blocks"], a["pooled"], None)
+
+
+def test_pool_refusals(lib):
+    assert pool(lib, n_blocks=0) == OK              # empty launch
+    assert pool(lib, tokens=3, n_blocks=0) == OK
+    assert pool(lib, raw=None) == NULL
+    assert pool(lib, w=None) == NULL
+    assert pool(lib, pooled=None) == NULL
+    assert pool(lib, tokens=-1) == EXTENT
+    assert pool(lib, first_block=-1) == EXTENT
+    assert pool(lib, n_blocks=-1) == EXTENT
+    assert pool(lib, n_blocks=17) == EXTENT
+    assert pool(lib, first_block=10, n_blocks=7) == EXTENT
+    assert pool(lib, first_block=17, n_blocks=0) == EXTENT
+    assert pool(lib, key_stride=127) == STRIDE
+    assert pool(lib, rd=63) == PARAM
+    assert pool(lib, rd=130) == PARAM
+    assert pool(lib, rd=-2) == PARAM
+    assert pool(lib, theta=0.0) == PARAM
+    assert pool(lib, theta=float("nan")) == PARAM
+    assert pool(lib, eps=-1e-6) == PARAM
+    assert pool(lib, eps=float("nan")) == PARAM
+    assert pool(lib, eps=float("inf")) == PARAM
+    assert pool(lib, tokens=2**62, key_stride=2**10, n_blocks=1) == CAP
+
+
+def score(lib, **kw):
+    a = dict(q=P, q_stride=512, pos=P, rows=8, w=P, rd=64, theta=1e4, eps=1e-6, pooled=P,
+             tokens=64, scores=P, score_cols=16, scores_len=128, status=P)
+    a.update(kw)
+    return lib.qsa_score_rows(a["q"], a["q_stride"], a["pos"], a["rows"], a["w"], a["rd"],
+                              a["theta"], a["eps"], a["pooled"], a["tokens"], a["scores"],
+                              a["score_cols"], a["scores_len"], a["status"], None)
+
+
+def test_score_refusals(lib):
+    assert score(lib, rows=0) == OK
+    assert score(lib, tokens=0, score_cols=0) == OK
+    for k in ("q", "pos", "w", "pooled", "scores", "status"):
+        assert score(lib, **{k: None}) == NULL, k
+    assert score(lib, rows=-1) == EXTENT
+    assert score(lib, tokens=-4) == EXTENT
+    assert score(lib, q_stride=511) == STRIDE
+    assert score(lib, score_cols=15) == STRIDE
+    assert score(lib, scores_len=127) == CAP
+    assert score(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
+    assert score(lib, rows=2**40, scores_len=2**62, score_cols=2**40) == CAP
+    assert score(lib, rd=65) == PARAM
+    assert score(lib, theta=-1.0) == PARAM
+    assert score(lib, eps=float("nan")) == PARAM
+
+
+def select(lib, **kw):
+    a = dict(scores=P, score_cols=16, scores_len=128, pos=P, rows=8, tokens=64, budget=2048,
+             mask=P, status=P)
+    a.update(kw)
+    return lib.qsa_select_mask(a["scores"], a["score_cols"], a["scores_len"], a["pos"], a["rows"],
+                               a["tokens"], a["budget"], a["mask"], a["status"], None)
+
+
+def test_select_refusals(lib):
+    assert select(lib, rows=0) == OK
+    assert select(lib, tokens=0, score_cols=0) == OK
+    for k in ("scores", "pos", "mask", "status"):
+        assert select(lib, **{k: None}) == NULL, k
+    assert select(lib, rows=-1) == EXTENT
+    assert select(lib, score_cols=-1) == EXTENT
+    for b in (0, -4, 2, 6, 2052, 4096):
+        assert select(lib, budget=b) == BUDGET, b
+    assert select(lib, score_cols=15) == STRIDE
+    assert select(lib, scores_len=127) == CAP
+    assert select(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
+    assert select(lib, rows=2**40, score_cols=16, scores_len=2**62) == CAP

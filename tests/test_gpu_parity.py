@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: pooled keys bit-exact; scores within 5e-3 absolute (the parity bound
+the score pages settle on); the selector fed the oracle's scores bit-exact;
+end-to-end masks may differ from the oracle's only at blocks whose oracle
+score lies within 5e-3 of the row's cut, and are structurally valid.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import (DEV, gpu_pool, gpu_scores, gpu_select, note, u16_dev, u16_host,
+                            workload)
+from tests.test_oracle_pins import check_structure
+
+pytestmark = pytest.mark.gpu
+
+SCORE_ATOL = 5e-3
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_pooled(wid):
+    w = workload(wid)
+    p = O.pool_keys(w["raw_keys"], w["k_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    return synth.apply_dups(p, w["dup_blocks"])
+
+
+def sample_rows(wid):
+    """Rows checked against the oracle: all, except the 8192-row chunk."""
+    w = workload(wid)
+    R = len(w["pos"])
+    if R <= 4096:
+        return np.arange(R)
+    rng = np.random.default_rng(9)
+    return np.unique(np.concatenate([[0, 1, R - 2, R - 1], rng.choice(R, 92, replace=False)]))
+
+
+def oracle_scores(wid, rows):
+    w = workload(wid)
+    qhat = O.prep_queries(w["queries"][rows], w["pos"][rows], w["q_norm_w"], w["rotary_dim"],
+                          w["theta"], w["eps"])
+    return O.score_rows(qhat, w["pos"][rows], oracle_pooled(wid), w["tokens"])
+
+
+def dense(score_list, cols):
+    out = np.full((len(score_list), max(cols, 1)), np.nan, dtype=np.float32)
+    for r, s in enumerate(score_list):
+        out[r, : len(s)] = s
+    return out
+
+
+# ------------------------------------------------------------------ pool ----
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_pool_bit_exact(wid):
+    w = workload(wid)
+    note(f"pool parity: workload {wid} ({w['name']}), tokens {w['tokens']}")
+    got = u16_host(gpu_pool(w))
+    want = O.pool_keys(w["raw_keys"], w["k_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    diff = np.nonzero(got != want)
+    assert len(diff[0]) == 0, (len(diff[0]), got[diff][:8], want[diff][:8], diff[0][:8], diff[1][:8])
+
+
+def test_pool_block_range_fused_row_stride_and_unaligned_stride():
+    w = workload(1)
+    T = w["tokens"]
+    want = O.pool_keys(w["raw_keys"], w["k_norm_w"], 64, 1e4, 1e-6)
+    # keys as the last 128 columns of a 640-wide fused row (4 query heads first)
+    fused = np.zeros((T, 640), dtype=np.uint16)
+    fused[:, 512:] = w["raw_keys"]
+    fused_dev = u16_dev(fused)
+    note("pool: fused 640-wide rows, blocks [37, 57)")
+    got = u16_host(gpu_pool(w, first_block=37, n_blocks=20, key_stride_view=fused_dev[:, 512:]))
+    assert np.array_equal(got[37:57], want[37:57])
+    assert np.all(got[:37] == 0x5A5A) and np.all(got[57:] == 0x5A5A)
+    # odd row stride (scalar loads)
+    odd = np.zeros((T, 129), dtype=np.uint16)
+    odd[:, :128] = w["raw_keys"]
+    note("pool: odd row stride 129")
+    got = u16_host(gpu_pool(w, key_stride_view=u16_dev(odd)))
+    assert np.array_equal(got, want)
+
+
+def test_pool_nan_key_poisons_only_its_block():
+    w = dict(workload(1))
+    raw = w["raw_keys"].copy()
+    raw[4 * 50 + 2, 7] = 0x7FC0
+    w["raw_keys"] = raw
+    got = O.f32_from_bf16(u16_host(gpu_pool(w)))
+    assert np.all(np.isnan(got[50]))
+    assert not np.any(np.isnan(np.delete(got, 50, axis=0)))
+
+
+# ---------------------------------------------------------------- select ----
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_select_on_oracle_scores_bit_exact(wid):
+    w = workload(wid)
+    rows = sample_rows(wid)
+    if wid == 5:
+        rows = rows[:48]
+    note(f"select parity on oracle scores: workload {wid}, {len(rows)} rows")
+    T = w["tokens"]
+    cols = T // 4
+    sc = dense(oracle_scores(wid, rows), cols)
+    pos = w["pos"][rows]
+    want, wst = O.select_mask(sc, cols, pos, T, w["budget"])
+    got, gst = gpu_select(sc, cols, pos, T, w["budget"])
+    assert gst == wst == 0
+    bad = [r for r in range(len(rows)) if not np.array_equal(got[r], want[r])]
+    assert not bad, (bad[:5], pos[bad[:5]])
+
+
+@pytest.mark.parametrize("kind", ["zeros", "ties", "lowbyte", "wild", "equal", "random", "poison"])
+def test_select_fixtures_bit_exact(kind):
+    scores, cols, pos, T = synth.selector_fixture(kind)
+    note(f"select fixture {kind}: rows {len(pos)}, tokens {T}")
+    for budget in (2048, 64, 4):
+        want, wst = O.select_mask(scores, cols, pos, T, budget)
+        got, gst = gpu_select(scores, cols, pos, T, budget)
+        assert gst == wst
+        bad = [r for r in range(len(pos)) if not np.array_equal(got[r], want[r])]
+        assert not bad, (budget, bad[:5], pos[bad[:5]])
+
+
+def test_select_spare_columns_ragged_tokens_and_bad_positions():
+    for T in (4099, 4098, 64, 5, 3, 1):
+        pos = np.array([T - 1, 0, T // 2, -1, T, 2 * T + 5], dtype=np.int32)
+        cols = T // 4 + 11
+        scores = np.full((len(pos), cols), np.nan, np.float32)
+        rng = np.random.default_rng(T)
+        for r, p in enumerate(pos):
+            n = (int(p) + 1) // 4 if 0 <= p < T else 0
+            scores[r, :n] = rng.standard_normal(n)
+        note(f"select ragged: tokens {T}")
+        want, wst = O.select_mask(scores, cols, pos, T, 64)
+        got, gst = gpu_select(scores, cols, pos, T, 64)
+        assert gst == wst == O.STATUS_BAD_POSITION
+        assert np.array_equal(got, want)
+
+
+def test_select_longest_supported_row():
+    T = 262147
+    pos = np.array([262146, 262145, 262144, 262143, 131071], dtype=np.int32)
+    for kind in ("random", "ties", "equal"):
+        scores, cols, pos2, _ = synth.selector_fixture(kind, positions=pos)
+        note(f"select longest rows: {kind}")
+        want, _ = O.select_mask(scores, cols, pos2, T, 2048)
+        got, st = gpu_select(scores, cols, pos2, T, 2048)
+        assert st == 0 and np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------- score ----
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_score_within_bound_and_prefix_only(wid):
+    w = workload(wid)
+    rows = sample_rows(wid)
+    T = w["tokens"]
+    cols = T // 4 + (7 if wid in (1, 3) else 0)
+    note(f"score parity: workload {wid}, {len(rows)} rows, score_cols {cols}")
+    pooled = u16_dev(oracle_pooled(wid))
+    sentinel = np.float32(-7.25)
+    got, st = gpu_scores(w, pooled, pos=w["pos"][rows], q=w["queries"][rows], score_cols=cols,
+                         sentinel=sentinel)
+    assert st == 0
+    want = oracle_scores(wid, rows)
+    worst = 0.0
+    for r, s in enumerate(want):
+        n = len(s)
+        assert np.all(got[r, n:] == sentinel), "wrote past the visible prefix"
+        if n:
+            d = np.abs(got[r, :n].astype(np.float64) - s)
+            worst = max(worst, float(d.max()))
+    note(f"  max |gpu - oracle| = {worst:.3e}")
+    assert worst <= SCORE_ATOL
+
+
+def test_score_duplicate_blocks_tie_exactly():
+    w = workload(1)
+    pooled = u16_dev(oracle_pooled(1))
+    got, _ = gpu_scores(w, pooled)
+    for b in w["dup_blocks"]:
+        vis = (w["pos"] + 1) // 4 > b
+        assert np.array_equal(got[vis, b].view(np.uint32), got[vis, b - 1].view(np.uint32))
+
+
+def test_score_nan_key_and_bad_positions():
+    w = workload(1)
+    pooled = oracle_pooled(1).copy()
+    pooled[50] = 0x7FC0
+    pos = np.array([199, 200, 202, 203, 204, 511, -3, 512, 700], dtype=np.int32)
+    q = w["queries"][: len(pos)]
+    got, st = gpu_scores(w, u16_dev(pooled), pos=pos, q=q)
+    assert st == O.STATUS_BAD_POSITION
+    for r, p in enumerate(pos):
+        if not 0 <= p < 512:
+            assert np.all(got[r] == np.float32(-7.25))
+            continue
+        n = (p + 1) // 4
+        if n > 50:
+            assert np.isnan(got[r, 50]) and np.all(np.isfinite(np.delete(got[r, :n], 50)))
+        else:
+            assert np.all(np.isfinite(got[r, :n]))
+
+
+# ------------------------------------------------------------ end to end ----
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_end_to_end_masks(wid):
+    w = workload(wid)
+    T = w["tokens"]
+    cols = T // 4
+    note(f"end to end: workload {wid}")
+    pooled_dev = gpu_pool(w)
+    if len(w["dup_blocks"]):
+        p = u16_host(pooled_dev)
+        pooled_dev = u16_dev(synth.apply_dups(p, w["dup_blocks"]))
+    scores, st = gpu_scores(w, pooled_dev)
+    assert st == 0
+    mask, st = gpu_select(scores, cols, w["pos"], T, w["budget"])
+    assert st == 0
+    rows = sample_rows(wid)
+    want_scores = oracle_scores(wid, rows)
+    want_dense = dense(want_scores, cols)
+    want_mask, _ = O.select_mask(want_dense, cols, w["pos"][rows], T, w["budget"])
+    loose = 0
+    for i, r in enumerate(rows):
+        p = int(w["pos"][r])
+        check_structure(mask[r], scores[r], p, T, w["budget"])
+        if np.array_equal(mask[r], want_mask[i]):
+            continue
+        n = (p + 1) // 4
+        keep = min(w["budget"] // 4, n)
+        s = want_scores[i]
+        cut = np.sort(s)[::-1][keep - 1]
+        gb = mask[r][: 4 * n].reshape(n, 4)[:, 0]
+        wb = want_mask[i][: 4 * n].reshape(n, 4)[:, 0]
+        diff = np.nonzero(gb != wb)[0]
+        assert np.all(np.abs(s[diff].astype(np.float64) - cut) <= SCORE_ATOL), (r, diff[:8])
+        loose += 1
+    note(f"  rows differing only at the cut: {loose} of {len(rows)}")
+
+
+def test_repeat_launches_are_bit_identical():
+    w = workload(3)
+    pooled_a = u16_host(gpu_pool(w))
+    pooled_b = u16_host(gpu_pool(w))
+    assert np.array_equal(pooled_a, pooled_b)
+    s1, _ = gpu_scores(w, u16_dev(pooled_a))
+    s2, _ = gpu_scores(w, u16_dev(pooled_a))
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    T = w["tokens"]
+    m1, _ = gpu_select(s1, T // 4, w["pos"], T, 2048)
+    for _ in range(3):
+        m2, _ = gpu_select(s1, T // 4, w["pos"], T, 2048)
+        assert np.array_equal(m1, m2)
