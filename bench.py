@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA indexer hot path on one MI355X.
+
+One step = qsa_pool_keys (every block) -> qsa_score_rows (every row) ->
+qsa_select_mask (every row) over one batch of a seeded synthetic workload,
+inputs resident in HBM.  W untimed warm-up steps, then K timed steps between
+two device synchronisations; per-kernel durations come from HIP events
+recorded on the launch stream around each call.
+
+Prints ONE JSON line.  `value` is scored (row, block) pairs per second of the
+whole step on the main workload (default: the 8192-row prefill chunk over a
+65536-token cache).  The same line carries select+mask microseconds per row
+on the 64k- and 256k-context decode workloads and on the one-row shapes, the
+roofline of the dominant kernel and the CPU oracle baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true", help="skip the decode and one-row figures")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU-oracle budget for the baseline sample")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# workload on the device
+# ----------------------------------------------------------------------------
+
+class Device:
+    def __init__(self, w, torch, qsa):
+        self.w, self.torch, self.qsa = w, torch, qsa
+        dev = "cuda:0"
+        np_ = __import__("numpy")
+        T = w["tokens"]
+        rows = len(w["pos"])
+        self.T, self.rows, self.cols = T, rows, T // 4
+        self.raw = torch.from_numpy(w["raw_keys"].view(np_.int16)).to(dev)
+        self.q = torch.from_numpy(w["queries"].reshape(rows, 512).view(np_.int16)).to(dev)
+        self.wk = torch.from_numpy(w["k_norm_w"].view(np_.int16)).to(dev)
+        self.wq = torch.from_numpy(w["q_norm_w"].view(np_.int16)).to(dev)
+        self.pos = torch.from_numpy(w["pos"].astype(np_.int32)).to(dev)
+        self.pooled = torch.empty((T // 4, 128), dtype=torch.int16, device=dev)
+        self.scores = torch.empty(rows * max(self.cols, 1), dtype=torch.float32, device=dev)
+        self.mask = torch.empty((rows, T), dtype=torch.uint8, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        n = (w["pos"].astype(np_.int64) + 1) // 4
+        self.pairs = int(n.sum())
+        self.nmax = int(n.max())
+
+    def pool(self):
+        w = self.w
+        self.qsa.qsa_pool_keys(self.raw, self.wk, w["rotary_dim"], w["theta"], w["eps"], self.pooled)
+
+    def score(self):
+        w = self.w
+        self.qsa.qsa_score_rows(self.q, self.pos, self.wq, w["rotary_dim"], w["theta"], w["eps"],
+                                self.pooled, self.T, self.scores, self.cols, self.status)
+
+    def select(self):
+        self.qsa.qsa_select_mask(self.scores, self.cols, self.pos, self.T, self.w["budget"],
+                                 self.mask, self.status)
+
+    # algorithmic bytes / flops per launch
+    def pool_bytes(self):
+        return (self.T // 4) * (4 * 256 + 256)
+
+    def score_bytes(self):
+        return self.nmax * 256 + self.rows * (1024 + 4) + 4 * self.pairs
+
+    def score_flops(self):
+        return 1024 * self.pairs
+
+    def select_bytes(self):
+        return 4 * self.pairs + self.rows * (self.T + 4)
+
+
+def time_steps(d: Device, steps: int, warmup: int, torch):
+    stages = (("pool", d.pool), ("score", d.score), ("select", d.select))
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    stream = torch.cuda.current_stream()
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)] for name, _ in stages}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for name, fn in stages:
+            a, b = ev[name][k]
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: [a.elapsed_time(b) * 1e3 for a, b in ev[name]] for name, _ in stages}  # us
+    return wall, per
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def kernel_report(d: Device, per_us):
+    mean = {k: sum(v) / len(v) for k, v in per_us.items()}
+    rep = {}
+    for name, b in (("pool", d.pool_bytes()), ("score", d.score_bytes()), ("select", d.select_bytes())):
+        t = mean[name]
+        gbs = b / (t * 1e-6) / 1e9
+        rep[name] = {"mean_us": round(t, 3), "median_us": round(median(per_us[name]), 3),
+                     "min_us": round(min(per_us[name]), 3), "max_us": round(max(per_us[name]), 3),
+                     "alg_bytes": b, "achieved_GBs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    tf = d.score_flops() / (mean["score"] * 1e-6) / 1e12
+    rep["score"]["alg_flops"] = d.score_flops()
+    rep["score"]["achieved_TFs"] = round(tf, 1)
+    rep["score"]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFS, 4)
+    return rep, mean
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
+    kernel's source is unchanged since they were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    entry = table.get(f"{kernel}:{workload}")
+    if not entry:
+        return None
+    src = os.path.join(ROOT, "sparse_attention_token_qsa_amd", "csrc", entry["source"])
+    if not os.path.exists(src) or source_hash(src) != entry["source_sha"]:
+        return None
+    return entry["hbm_bytes_per_launch"]
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w, budget_s: float):
+    import numpy as np
+    import oracle as O
+    T = w["tokens"]
+    pos = w["pos"]
+    rows_total = len(pos)
+    t0 = time.perf_counter()
+    pooled = O.pool_keys(w["raw_keys"], w["k_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    t_pool = time.perf_counter() - t0
+    # score + select per row, on as many rows as the budget allows
+    rng = np.random.default_rng(0)
+    order = rng.permutation(rows_total)
+    done, pairs, t_rows = 0, 0, 0.0
+    cols = T // 4
+    while done < rows_total and (t_pool + t_rows) < budget_s:
+        r = order[done: done + 8]
+        t1 = time.perf_counter()
+        qhat = O.prep_queries(w["queries"][r], pos[r], w["q_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+        sc = O.score_rows(qhat, pos[r], pooled, T)
+        dense = np.zeros((len(r), cols), dtype=np.float32)
+        for i, s in enumerate(sc):
+            dense[i, : len(s)] = s
+        O.select_mask(dense, cols, pos[r], T, w["budget"])
+        t_rows += time.perf_counter() - t1
+        pairs += int(sum(len(s) for s in sc))
+        done += len(r)
+    t_step = t_pool * done / rows_total + t_rows
+    cores = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": pairs / t_step, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{w['name']}: oracle pool of all {T // 4} blocks ({t_pool:.2f} s, "
+                       f"charged pro rata), then prep+score+select of {done} of {rows_total} "
+                       f"rows ({pairs} pairs, {t_rows:.2f} s); numpy, f64 BLAS matmul over "
+                       f"{cores} threads; {model}")}
+
+
+# ----------------------------------------------------------------------------
+
+def side_figures(torch, qsa, synth):
+    """select+mask us/row on the 64k/256k decode workloads and the one-row
+    64k/256k shapes; per-kernel event means over 20 launches after 5 warm-ups."""
+    out = {}
+    for key, w in (("decode_64k_x64", synth.make_workload(3)),
+                   ("decode_256k_x16", synth.make_workload(4)),
+                   ("one_row_64k", synth.single_row(3, 65535)),
+                   ("one_row_256k", synth.single_row(4, 262143))):
+        d = Device(w, torch, qsa)
+        wall, per = time_steps(d, 20, 5, torch)
+        rep, mean = kernel_report(d, per)
+        out[key] = {"rows": d.rows, "tokens": d.T, "pairs": d.pairs,
+                    "select_mask_us_per_row": round(mean["select"] / d.rows, 3),
+                    "step_us_events": round(sum(mean.values()), 2),
+                    "pairs_per_s": round(d.pairs / (sum(mean.values()) * 1e-6), 1),
+                    "kernels": rep}
+        del d
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the indexer path here "
+              f"is a single-GPU kernel set with no cross-GPU sharding.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_attention_token_qsa_amd as qsa
+    import synth
+
+    qsa.load()
+    w = synth.make_workload(args.workload)
+    d = Device(w, torch, qsa)
+    wall, per = time_steps(d, args.steps, args.warmup, torch)
+    st = qsa.check_status(d.status)
+    if st != 0:
+        raise RuntimeError(f"device status {st} on a clean workload")
+    rep, mean = kernel_report(d, per)
+    ms_per_step = wall / args.steps * 1e3
+    value = d.pairs / (wall / args.steps)
+
+    # dominant kernel and its roofline
+    dom = max(mean, key=mean.get)
+    if dom == "score":
+        t_hbm = d.score_bytes() / (HBM_PEAK_GBS * 1e9)
+        t_mfma = d.score_flops() / (MFMA_BF16_PEAK_TFS * 1e12)
+        bound = "mfma" if t_mfma > t_hbm else "hbm"
+    else:
+        bound = "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": rep["score"]["achieved_TFs"], "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": rep["score"]["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": rep[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": rep[dom]["hbm_frac"]}
+    roof["kernel"] = dom
+    roof["traffic"] = traffic_for(dom, w["name"])
+
+    side = {} if args.no_side else side_figures(torch, qsa, synth)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": "scored (row,block) pairs/s + select+mask us/row at 64k and 256k ctx",
+        "value": round(value, 1),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "rows": d.rows, "tokens": d.T, "budget": w["budget"],
+                   "heads": 4, "head_dim": 128, "rotary_dim": w["rotary_dim"],
+                   "pairs_per_step": d.pairs, "parallelism": "single-gpu"},
+        "select_mask_us_per_row": {
+            "64k": side.get("decode_64k_x64", {}).get("select_mask_us_per_row"),
+            "256k": side.get("decode_256k_x16", {}).get("select_mask_us_per_row"),
+            "one_row_64k": side.get("one_row_64k", {}).get("select_mask_us_per_row"),
+            "one_row_256k": side.get("one_row_256k", {}).get("select_mask_us_per_row"),
+            "main_workload": round(mean["select"] / d.rows, 4),
+        },
+        "kernels": rep,
+        "roofline": roof,
+        "side_workloads": side,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
