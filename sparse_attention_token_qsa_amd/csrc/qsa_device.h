@@ -75,3 +75,75 @@ __device__ __forceinline__ float rope_channel(float x, float xp, float c, float 
 }
 
 }  // namespace qsa
+
+namespace qsa {
+
+// ---- wavefront primitives (64 lanes) built on DPP row operations --------
+//
+// update_dpp(old, v, ctrl, rows, banks, bound_ctrl=false) returns v from the
+// lane `ctrl` selects, or `old` where that lane is outside the row or the row
+// is masked off.  0x111/0x112/0x114/0x118 = row_shr 1/2/4/8 (within 16-lane
+// rows), 0x142 = row_bcast 15 (last lane of each row to the next row),
+// 0x143 = row_bcast 31 (lane 31 to rows 2 and 3).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xF, false));
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += dpp_u32<0x111>(0u, v);
+  v += dpp_u32<0x112>(0u, v);
+  v += dpp_u32<0x114>(0u, v);
+  v += dpp_u32<0x118>(0u, v);
+  v += dpp_u32<0x142, 0xA>(0u, v);
+  v += dpp_u32<0x143, 0xC>(0u, v);
+  return v;
+}
+
+// Maximum / minimum over the wave, returned in every lane (uniform).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111>(v, v));
+  v = max(v, dpp_u32<0x112>(v, v));
+  v = max(v, dpp_u32<0x114>(v, v));
+  v = max(v, dpp_u32<0x118>(v, v));
+  v = max(v, dpp_u32<0x142, 0xA>(v, v));
+  v = max(v, dpp_u32<0x143, 0xC>(v, v));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0x111>(v, v));
+  v = min(v, dpp_u32<0x112>(v, v));
+  v = min(v, dpp_u32<0x114>(v, v));
+  v = min(v, dpp_u32<0x118>(v, v));
+  v = min(v, dpp_u32<0x142, 0xA>(v, v));
+  v = min(v, dpp_u32<0x143, 0xC>(v, v));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// 64-bit maximum / minimum over the wave (uniform result).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = wave_max_u32(static_cast<uint32_t>(v >> 32));
+  const uint32_t lo = wave_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  const uint32_t hi = wave_min_u32(static_cast<uint32_t>(v >> 32));
+  const uint32_t lo = wave_min_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0xFFFFFFFFu);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Order LDS traffic of one wave against itself (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace qsa

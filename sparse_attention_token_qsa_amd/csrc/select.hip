@@ -7,17 +7,28 @@
 // their 4 tokens and on the tail.  A row under the budget keeps its whole
 // visible prefix.  A non-finite score in the row's prefix is refused.
 //
-// One workgroup per row; the row's scores live in registers as order-keys
-// (KPT per thread, block b = tid + j * NT) for the whole selection:
-//  1. four 8-bit LDS histogram passes over the keys matching the prefix found
-//     so far give the keep-th largest key K* and the rank `need` of the cut
-//     inside the run of keys equal to K*;
-//  2. if fewer than all equal keys are taken, the ascending-index tie fill
-//     picks the need-th equal key in block order: per-chunk wavefront
-//     ballots count the equal keys, a prefix walk finds the chunk, the wave
-//     and the lane; that lane's block index is the last taken one, B*;
-//  3. block b is kept iff key_b > K* or (key_b == K* and b <= B*); each thread
-//     writes its blocks' 4 mask bytes, then the tail and the zero run.
+// Order as one integer.  Each visible block gets the 64-bit composite
+//   C(b) = key(score_b) << 32 | (0xFFFFFFFF - b),
+// with key() the order-preserving u32 map of a finite float (-0.0 folded onto
+// +0.0).  The canonical order is C descending and all C are distinct, so the
+// kept set is exactly {b : C(b) >= C*} where C* is the keep-th largest
+// composite: selection is one threshold, ties included.
+//
+// One workgroup per row; the row's keys live in registers (KPT per thread).
+//  1. Long rows (1024 threads): every thread's largest key is a distinct
+//     key; taking in each wave the r-th largest of the 64 thread maxima,
+//     r = ceil(keep / waves), and the minimum L of those over the waves, at
+//     least keep keys are >= L.  So C* >= L << 32 and only keys >= L can be
+//     kept.  They are compacted into LDS (typically ~1k of 16k-64k).
+//  2. Radix select of C* over the candidates (the compacted list, or all
+//     keys when the list would overflow or the row is short), 8 bits per
+//     pass starting just below the common prefix of the candidates' smallest
+//     and largest composite, so the first histogram is not crowded into the
+//     few exponent bins the scores occupy.  A pass ends the search early once
+//     every candidate of the chosen bin is taken; the returned bin floor then
+//     separates the candidates, and `lowkey` excludes the non-candidates.
+//  3. Each thread writes its blocks' mask bytes (16 bytes per 4 blocks), the
+//     tail and the zero run from the same loop.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -32,10 +43,25 @@ struct SelectArgs {
   int keep_max;
   uint8_t* mask;
   int32_t* status;
-  int words;  // mask rows are 4-byte aligned: write them as u32 words
 };
 
-// Mask word covering tokens [4w, 4w+4): 1 for every token t <= last.
+constexpr int kCandCap = 4096;
+
+// A register copy the compiler cannot see through: values derived from it
+// are computed where they are used instead of being hoisted and kept live
+// (64 keys per thread leave no room for 64 precomputed 64-bit composites).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, int b) {
+  return (static_cast<uint64_t>(key) << 32) |
+         static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(b));
+}
+
+// Mask word of the token group [4w, 4w+4) outside the selected blocks: 1 for
+// every token t <= last.
 __device__ __forceinline__ uint32_t prefix_word(int64_t w, int64_t last) {
   const int64_t t0 = 4 * w;
   uint32_t v = 0;
@@ -44,94 +70,72 @@ __device__ __forceinline__ uint32_t prefix_word(int64_t w, int64_t last) {
   return v;
 }
 
-// Bytes [from, tokens) of a mask row: 1 for t <= last, else 0.
-template <int NT>
-__device__ __forceinline__ void write_run(uint8_t* mrow, int64_t tokens, int64_t from_word,
-                                          int64_t last, bool words) {
-  if (words) {
-    const int64_t nwords = tokens >> 2;
-    for (int64_t w = from_word + threadIdx.x; w < nwords; w += NT)
-      reinterpret_cast<uint32_t*>(mrow)[w] = prefix_word(w, last);
-    const int64_t rest = tokens & 3;
-    if (rest && threadIdx.x == 0)
-      for (int64_t t = tokens - rest; t < tokens; ++t) mrow[t] = t <= last ? 1 : 0;
+// Bytes [0, tokens) of a mask row: 1 for t <= last, else 0.
+template <int NT, bool VEC>
+__device__ __forceinline__ void write_prefix_row(uint8_t* mrow, int64_t tokens, int64_t last) {
+  if constexpr (VEC) {
+    const int64_t chunks = tokens >> 4;
+    for (int64_t c = threadIdx.x; c < chunks; c += NT) {
+      uint4 v;
+      v.x = prefix_word(4 * c + 0, last);
+      v.y = prefix_word(4 * c + 1, last);
+      v.z = prefix_word(4 * c + 2, last);
+      v.w = prefix_word(4 * c + 3, last);
+      reinterpret_cast<uint4*>(mrow)[c] = v;
+    }
   } else {
-    for (int64_t t = 4 * from_word + threadIdx.x; t < tokens; t += NT) mrow[t] = t <= last ? 1 : 0;
+    for (int64_t t = threadIdx.x; t < tokens; t += NT) mrow[t] = t <= last ? 1 : 0;
   }
 }
 
-template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
+// Radix search for the keep-th largest composite among a candidate set.
+// `each(f)` calls f(composite) for every candidate this thread owns.
+// Returns C* (or the floor of a bin whose candidates are all taken: the same
+// kept set among the candidates).  All threads return the same value.
+template <int NT, typename Each>
+__device__ uint64_t radix_threshold(Each each, uint32_t k, uint32_t* hist, uint64_t* red64) {
   constexpr int NW = NT / 64;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t chunk_cnt[KPT];
-  __shared__ uint32_t wave_cnt[NW];
-  __shared__ uint32_t sh_digit, sh_above, sh_equal, sh_chunk, sh_need, sh_wave;
-  __shared__ int sh_bstar;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const int64_t T = a.tokens;
-  uint8_t* mrow = a.mask + row * T;
-  const int64_t p = a.pos[row];
-
-  if (p < 0 || p >= T) {
-    write_run<NT>(mrow, T, 0, -1, a.words);
-    if (tid == 0) atomicOr(a.status, 1);
-    return;
-  }
-  const int64_t n = (p + 1) / kRatio;
-  const int64_t keep = n < a.keep_max ? n : a.keep_max;
-
-  // Load the visible prefix as order-keys.  A finite score's key is at least
-  // 0x00800000, so key 0 marks an absent slot and is never counted.
-  const float* srow = a.scores + row * a.score_cols;
-  const int n32 = static_cast<int>(n);
-  uint32_t key[KPT];
-  int bad = 0;
-  if (n32 > 0) {
-    // Every load is issued before any is consumed; slots past the prefix
-    // re-read the last visible score and are then discarded.
-    float sv[KPT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint32_t sh_digit, sh_above, sh_count;
+  // smallest and largest candidate composite
+  uint64_t lo = ~0ull, hi = 0ull;
+  each([&](uint64_t c) {
+    lo = c < lo ? c : lo;
+    hi = c > hi ? c : hi;
+  });
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int b = tid + j * NT;
-      sv[j] = srow[b < n32 ? b : n32 - 1];
-    }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t l2 = __shfl_xor(lo, off), h2 = __shfl_xor(hi, off);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    red64[wave] = lo;
+    red64[NW + wave] = hi;
+  }
+  __syncthreads();
+  lo = red64[0];
+  hi = red64[NW];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool live = tid + j * NT < n32;
-      bad |= live && !is_finite_bits(sv[j]);
-      key[j] = live ? score_key(sv[j]) : 0u;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = 0u;
+  for (int w = 1; w < NW; ++w) {
+    lo = red64[w] < lo ? red64[w] : lo;
+    hi = red64[NW + w] > hi ? red64[NW + w] : hi;
   }
-  if (__syncthreads_or(bad)) {
-    write_run<NT>(mrow, T, 0, -1, a.words);
-    if (tid == 0) atomicOr(a.status, 2);
-    return;
-  }
-  if (n <= keep) {  // every block kept: the visible prefix [0, p]
-    write_run<NT>(mrow, T, 0, p, a.words);
-    return;
-  }
-
-  // ---- radix select of the keep-th largest key, 8 bits per pass, MSB first.
-  uint32_t prefix = 0u, pmask = 0u, k = static_cast<uint32_t>(keep);
-#pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  if (lo == hi) return hi;  // a single candidate
+  int top = 63 - __clzll(lo ^ hi);  // highest bit that differs among candidates
+  uint64_t prefix = hi & ~((2ull << top) - 1ull);  // the shared bits above `top`
+  while (true) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const int width = top - shift + 1;
+    const uint64_t himask = ~((2ull << top) - 1ull);  // bits above the digit
     for (int i = tid; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+    each([&](uint64_t c) {
+      if ((c & himask) == prefix) atomicAdd(&hist[(c >> shift) & ((1u << width) - 1u)], 1u);
+    });
     __syncthreads();
     if (wave == 0) {
-      // lane l owns bins 4l..4l+3; suffix sums from the top bin down
       uint32_t h[4], tot = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -144,102 +148,243 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
         const uint32_t v = __shfl_down(incl, off);
         if (lane + off < 64) incl += v;
       }
-      uint32_t above = incl - tot;  // keys in bins of higher lanes
+      uint32_t above = incl - tot;
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         if (above < k && above + h[i] >= k) {
           sh_digit = 4 * lane + i;
           sh_above = above;
-          sh_equal = h[i];
+          sh_count = h[i];
         }
         above += h[i];
       }
     }
     __syncthreads();
-    prefix |= sh_digit << shift;
-    pmask |= 255u << shift;
-    k -= sh_above;
+    const uint32_t d = sh_digit, above = sh_above, count = sh_count;
+    __syncthreads();  // hist and the sh_ words are rewritten by the next pass
+    prefix |= static_cast<uint64_t>(d) << shift;
+    k -= above;
+    if (count == k || shift == 0) return prefix;  // every candidate of bin d is taken
+    top = shift - 1;
   }
-  const uint32_t kstar = prefix;
-  const uint32_t need = k;  // taken among the keys equal to K*, 1..equal
-  const uint32_t equal = sh_equal;
+}
 
-  int bstar = 0x7FFFFFFF;
-  if (need < equal) {
-    // ---- ascending-index tie fill: the need-th key equal to K* in block order.
-    for (int j = tid; j < KPT; j += NT) chunk_cnt[j] = 0u;
-    __syncthreads();
+template <int NT, int KPT, bool VEC>
+__global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
+  constexpr int NW = NT / 64;
+  constexpr bool kPrefilter = (NT == 1024);
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t red[NW];
+  __shared__ uint64_t red64[2 * NW];
+  __shared__ uint64_t cand[kPrefilter ? kCandCap : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t T = a.tokens;
+  uint8_t* mrow = a.mask + row * T;
+  const int64_t p = a.pos[row];
+
+  if (p < 0 || p >= T) {
+    write_prefix_row<NT, VEC>(mrow, T, -1);
+    if (tid == 0) atomicOr(a.status, 1);
+    return;
+  }
+  const int n = static_cast<int>((p + 1) / kRatio);
+  const int keep = n < a.keep_max ? n : a.keep_max;
+
+  // Block of register slot j: 4 consecutive blocks per 16-byte group when
+  // vectorised, else one block per slot.
+  auto blk = [&](int j) { return VEC ? 4 * (tid + (j >> 2) * NT) + (j & 3) : tid + j * NT; };
+
+  // ---- load the visible prefix as order-keys (0 = absent; a finite score's
+  // key is at least 0x00800000).
+  const float* srow = a.scores + row * a.score_cols;
+  uint32_t key[KPT];
+  int bad = 0;
+  if (n > 0) {
+    if constexpr (VEC) {
+      const float4* s4 = reinterpret_cast<const float4*>(srow);
+      const int qlast = (n - 1) >> 2;
+      float4 v[KPT / 4];
+#pragma unroll
+      for (int g = 0; g < KPT / 4; ++g) {
+        const int q = tid + g * NT;
+        v[g] = s4[q < qlast ? q : qlast];
+      }
+#pragma unroll
+      for (int g = 0; g < KPT / 4; ++g) {
+        const float e[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool live = blk(4 * g + i) < n;
+          bad |= live && !is_finite_bits(e[i]);
+          key[4 * g + i] = live ? score_key(e[i]) : 0u;
+        }
+      }
+    } else {
+      float sv[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int b = blk(j);
+        sv[j] = srow[b < n ? b : n - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool live = blk(j) < n;
+        bad |= live && !is_finite_bits(sv[j]);
+        key[j] = live ? score_key(sv[j]) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = 0u;
+  }
+  if (__syncthreads_or(bad)) {
+    write_prefix_row<NT, VEC>(mrow, T, -1);
+    if (tid == 0) atomicOr(a.status, 2);
+    return;
+  }
+  if (n <= keep) {  // every block kept: the visible prefix [0, p]
+    write_prefix_row<NT, VEC>(mrow, T, p);
+    return;
+  }
+
+  // ---- threshold composite C*.  The search may return the floor of the bin
+  // holding C*; it separates the candidates exactly, and `lowkey` (the
+  // prefilter bound, or 1 to exclude absent slots) excludes the rest.
+  uint64_t cstar = 0;
+  uint32_t lowkey = 1u;
+  bool done = false;
+  if constexpr (kPrefilter) {
+    if (n >= 4 * NT) {  // every thread owns at least one visible block
+      uint32_t tmax = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) tmax = key[j] > tmax ? key[j] : tmax;
+      // r-th largest thread maximum of this wave: bitonic sort, descending
+      const int r = (keep + NW - 1) / NW;
+      uint32_t v = tmax;
+#pragma unroll
+      for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride >= 1; stride >>= 1) {
+          const uint32_t o = __shfl_xor(v, stride);
+          const bool desc = ((lane & size) == 0) || size == 64;
+          const bool lower = ((lane & stride) == 0);
+          const bool take_max = (desc == lower);
+          v = take_max ? (o > v ? o : v) : (o < v ? o : v);
+        }
+      }
+      const uint32_t lw = __shfl(v, r - 1);
+      __syncthreads();
+      if (lane == 0) red[wave] = lw;
+      __syncthreads();
+      uint32_t L = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) L = red[w] < L ? red[w] : L;
+      // count and compact the candidates key >= L
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) mine += key[j] >= L ? 1u : 0u;
+      uint32_t incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      __syncthreads();
+      if (lane == 63) red[wave] = incl;
+      __syncthreads();
+      uint32_t base = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        base += w < wave ? red[w] : 0u;
+        total += red[w];
+      }
+      if (total <= static_cast<uint32_t>(kCandCap)) {
+        uint32_t at = base + incl - mine;
+        const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
+          const uint32_t kk = opaque(key[j]);
+          if (kk >= L) cand[at++] = composite(kk, b);
+        }
+        __syncthreads();
+        const int c = static_cast<int>(total);
+        cstar = radix_threshold<NT>(
+            [&](auto f) {
+              for (int i = tid; i < c; i += NT) f(cand[i]);
+            },
+            static_cast<uint32_t>(keep), hist, red64);
+        lowkey = L;
+        done = true;
+      }
+    }
+  }
+  if (!done) {
+    cstar = radix_threshold<NT>(
+        [&](auto f) {
+          // An opaque copy of the thread index: the composites are rebuilt in
+          // every pass instead of being hoisted into 2*KPT live registers.
+          int t = tid;
+          asm volatile("" : "+v"(t));
+#pragma unroll
+          for (int j = 0; j < KPT; ++j) {
+            const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
+            const uint32_t kk = opaque(key[j]);
+            if (kk != 0u) f(composite(kk, b));
+          }
+        },
+        static_cast<uint32_t>(keep), hist, red64);
+  }
+
+  // ---- mask: kept blocks, the tail [4n, p] and zeros; every 16-byte chunk
+  // of the row belongs to exactly one register group.  C(b) >= C* splits
+  // into 32-bit tests: key > K*, or key == K* and b <= B*.
+  const uint32_t khi = static_cast<uint32_t>(cstar >> 32);
+  const int64_t blim = 0xFFFFFFFFll - static_cast<int64_t>(static_cast<uint32_t>(cstar));
+  auto kept = [&](uint32_t kk, int b) {
+    return kk >= lowkey && (kk > khi || (kk == khi && static_cast<int64_t>(b) <= blim));
+  };
+  if constexpr (VEC) {
+#pragma unroll
+    for (int g = 0; g < KPT / 4; ++g) {
+      const int q = tid + g * NT;
+      if (static_cast<int64_t>(q) * 16 < T) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = 4 * q + i;
+          const uint32_t kk = opaque(key[4 * g + i]);
+          wv[i] = b < n ? (kept(kk, b) ? 0x01010101u : 0u) : prefix_word(b, p);
+        }
+        reinterpret_cast<uint4*>(mrow)[q] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+    }
+  } else {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint64_t bal = __ballot(key[j] == kstar);
-      if (lane == 0 && bal) atomicAdd(&chunk_cnt[j], static_cast<uint32_t>(__popcll(bal)));
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t cum = 0;
-      for (int j = 0; j < KPT; ++j) {
-        if (cum + chunk_cnt[j] >= need) {
-          sh_chunk = j;
-          sh_need = need - cum;
-          break;
-        }
-        cum += chunk_cnt[j];
-      }
-    }
-    __syncthreads();
-    const int jstar = static_cast<int>(sh_chunk);
-    bool eq_here = false;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (j == jstar) eq_here = key[j] == kstar;
-    const uint64_t bal = __ballot(eq_here);
-    if (lane == 0) wave_cnt[wave] = static_cast<uint32_t>(__popcll(bal));
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t cum = 0;
-      const uint32_t need2 = sh_need;
-      for (int w = 0; w < NW; ++w) {
-        if (cum + wave_cnt[w] >= need2) {
-          sh_wave = w;
-          sh_need = need2 - cum;
-          break;
-        }
-        cum += wave_cnt[w];
-      }
-    }
-    __syncthreads();
-    if (wave == static_cast<int>(sh_wave) && eq_here) {
-      const uint64_t below = bal & ((1ull << lane) - 1ull);
-      if (static_cast<uint32_t>(__popcll(below)) + 1u == sh_need)
-        sh_bstar = tid + jstar * NT;
-    }
-    __syncthreads();
-    bstar = sh_bstar;
-  }
-
-  // ---- mask: kept blocks, then the tail [4n, p] and zeros to the end.
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int b = tid + j * NT;
-    if (key[j] != 0u) {
-      const bool kept = key[j] > kstar || (key[j] == kstar && b <= bstar);
-      if (a.words) {
-        reinterpret_cast<uint32_t*>(mrow)[b] = kept ? 0x01010101u : 0u;
-      } else {
-        const uint8_t v = kept ? 1 : 0;
+      const int b = blk(j);
+      if (b < n) {
+        const uint8_t v = kept(opaque(key[j]), b) ? 1 : 0;
         mrow[4 * b] = v;
         mrow[4 * b + 1] = v;
         mrow[4 * b + 2] = v;
         mrow[4 * b + 3] = v;
       }
     }
+    for (int64_t t = 4 * static_cast<int64_t>(n) + tid; t < T; t += NT) mrow[t] = t <= p ? 1 : 0;
   }
-  write_run<NT>(mrow, T, n, p, a.words);
 }
 
 template <int NT, int KPT>
-hipError_t launch_select_t(const SelectArgs& a, int64_t rows, hipStream_t stream) {
-  select_kernel<NT, KPT><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+hipError_t launch_select_t(const SelectArgs& a, int64_t rows, bool vec, hipStream_t stream) {
+  if (vec)
+    select_kernel<NT, KPT, true><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+  else
+    select_kernel<NT, KPT, false><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -256,18 +401,18 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
   a.keep_max = keep_max;
   a.mask = mask;
   a.status = status;
-  a.words = (tokens % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 4 == 0);
+  // 16-byte loads of 4 scores and 16-byte mask stores of 4 blocks
+  const bool vec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0) &&
+                   (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
   const int64_t nmax = tokens / kRatio;
   if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (nmax <= 256) return launch_select_t<256, 1>(a, rows, stream);
-  if (nmax <= 512) return launch_select_t<256, 2>(a, rows, stream);
-  if (nmax <= 1024) return launch_select_t<256, 4>(a, rows, stream);
-  if (nmax <= 2048) return launch_select_t<256, 8>(a, rows, stream);
-  if (nmax <= 4096) return launch_select_t<256, 16>(a, rows, stream);
-  if (nmax <= 8192) return launch_select_t<1024, 8>(a, rows, stream);
-  if (nmax <= 16384) return launch_select_t<1024, 16>(a, rows, stream);
-  if (nmax <= 32768) return launch_select_t<1024, 32>(a, rows, stream);
-  if (nmax <= 65536) return launch_select_t<1024, 64>(a, rows, stream);
+  if (nmax <= 1024) return launch_select_t<256, 4>(a, rows, vec, stream);
+  if (nmax <= 2048) return launch_select_t<256, 8>(a, rows, vec, stream);
+  if (nmax <= 4096) return launch_select_t<256, 16>(a, rows, vec, stream);
+  if (nmax <= 8192) return launch_select_t<1024, 8>(a, rows, vec, stream);
+  if (nmax <= 16384) return launch_select_t<1024, 16>(a, rows, vec, stream);
+  if (nmax <= 32768) return launch_select_t<1024, 32>(a, rows, vec, stream);
+  if (nmax <= 65536) return launch_select_t<1024, 64>(a, rows, vec, stream);
   return hipErrorInvalidValue;
 }
 
