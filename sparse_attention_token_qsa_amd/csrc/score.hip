@@ -59,11 +59,13 @@ struct ScoreSmem {
   static constexpr int WN = 4 / WM;
   static constexpr int RG = 8 * WM;           // query rows per workgroup
   static constexpr int TILE = kNPerWave * WN;  // blocks per iteration
+  // prologue: normed + roped queries, the norm's partner buffer, cos/sin
   static constexpr int kQBytes = RG * 4 * kPitch * 2;
-  static constexpr int kBBytes = TILE * kPitch * 2;
-  static constexpr int kPrologueBytes = 16 * kHeadDim * 4 + RG * kMaxHalfRotary * 8;
-  static constexpr int kUnionBytes = kBBytes > kPrologueBytes ? kBBytes : kPrologueBytes;
-  static constexpr int kBytes = kQBytes + kUnionBytes;
+  static constexpr int kPrologueBytes = kQBytes + 16 * kHeadDim * 4 + RG * kMaxHalfRotary * 8;
+  // block loop: two key tiles
+  static constexpr int kTileBytes = TILE * kPitch * 2;
+  static constexpr int kBytes = kPrologueBytes > 2 * kTileBytes ? kPrologueBytes : 2 * kTileBytes;
+  static constexpr int kChunks = TILE * 16 / kScoreThreads;  // 16-byte loads per thread per tile
 };
 
 template <int WM>
@@ -77,10 +79,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   __shared__ int sh_nmax;
 
   uint16_t(*qs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem);
-  unsigned char* uni = smem + S::kQBytes;
-  uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(uni);
-  float(*ybuf)[kHeadDim] = reinterpret_cast<float(*)[kHeadDim]>(uni);
-  float2(*csq)[kMaxHalfRotary] = reinterpret_cast<float2(*)[kMaxHalfRotary]>(uni + 16 * kHeadDim * 4);
+  float(*ybuf)[kHeadDim] = reinterpret_cast<float(*)[kHeadDim]>(smem + S::kQBytes);
+  float2(*csq)[kMaxHalfRotary] =
+      reinterpret_cast<float2(*)[kMaxHalfRotary]>(smem + S::kQBytes + 16 * kHeadDim * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,6 +115,40 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   if (blk_begin >= nmax) return;  // uniform across the workgroup
   int64_t blk_end = (split + 1) * a.tiles_per_split * TILE;
   if (blk_end > nmax) blk_end = nmax;
+
+  // ---- key tiles: this thread's 16-byte chunks of a tile, loaded to
+  // registers one tile ahead of the MFMAs that read them from LDS.
+  uint4 pre[S::kChunks];
+  auto fetch = [&](int64_t nb0) {
+#pragma unroll
+    for (int i = 0; i < S::kChunks; ++i) {
+      const int idx = tid + i * kScoreThreads;
+      const int64_t bb = nb0 + (idx >> 4);
+      const int c = idx & 15;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (bb < blk_end) {
+        const uint16_t* src = a.pooled + bb * kHeadDim + 8 * c;
+        if (a.pooled_vec) {
+          v = *reinterpret_cast<const uint4*>(src);
+        } else {
+          v.x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
+          v.y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
+          v.z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
+          v.w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
+        }
+      }
+      pre[i] = v;
+    }
+  };
+  auto stash = [&](int buf) {
+    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * S::kTileBytes);
+#pragma unroll
+    for (int i = 0; i < S::kChunks; ++i) {
+      const int idx = tid + i * kScoreThreads;
+      *reinterpret_cast<uint4*>(&bs[idx >> 4][8 * (idx & 15)]) = pre[i];
+    }
+  };
+  fetch(blk_begin);  // in flight during the query prep
 
   // ---- query prep: (1 + w) RMSNorm per head, then RoPE at the row's position.
   const int rd = a.rp.rotary_dim;
@@ -191,50 +226,54 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   for (int ks = 0; ks < 8; ++ks)
     afrag[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[mrow][16 * ks + khalf]);
 
-  // ---- block loop
+  // per-lane output rows: this lane holds rows 8m + 2 q4 + (lane >> 5)
+  float* orow[4];
+  int ovis[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int lr = 8 * m + 2 * q4 + (lane >> 5);
+    orow[q4] = a.scores + (row0 + lr) * a.score_cols;
+    ovis[q4] = nvis[lr];
+  }
+  __syncthreads();  // every wave holds its A fragments: the LDS becomes key tiles
+  stash(0);
+  __syncthreads();
+
+  // ---- block loop: MFMAs on tile t (LDS) while tile t+1 is fetched
+  int buf = 0;
   for (int64_t nb0 = blk_begin; nb0 < blk_end; nb0 += TILE) {
-    __syncthreads();  // the previous tile (or the prologue's LDS) is no longer read
-    for (int idx = tid; idx < TILE * 16; idx += kScoreThreads) {
-      const int r = idx >> 4;
-      const int c = idx & 15;
-      const int64_t bb = nb0 + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (bb < blk_end) {
-        const uint16_t* src = a.pooled + bb * kHeadDim + 8 * c;
-        if (a.pooled_vec) {
-          v = *reinterpret_cast<const uint4*>(src);
-        } else {
-          v.x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
-          v.y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
-          v.z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
-          v.w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
-        }
-      }
-      *reinterpret_cast<uint4*>(&bs[r][8 * c]) = v;
+    const bool more = nb0 + TILE < blk_end;
+    if (more) fetch(nb0 + TILE);
+    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * S::kTileBytes);
+    const int col0 = ng * kNPerWave + (lane & 31);
+    f32x16_t acc0, acc1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc0[v] = 0.0f;
+      acc1[v] = 0.0f;
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&bs[col0][16 * ks + khalf]);
+      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&bs[col0 + 32][16 * ks + khalf]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], b1, acc1, 0, 0, 0);
+    }
+    const int blk0 = static_cast<int>(nb0) + col0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float s0 = relu_keep_nan(acc0[4 * q4 + 0]) + relu_keep_nan(acc0[4 * q4 + 1]);
+      s0 = s0 + relu_keep_nan(acc0[4 * q4 + 2]);
+      s0 = s0 + relu_keep_nan(acc0[4 * q4 + 3]);
+      float s1 = relu_keep_nan(acc1[4 * q4 + 0]) + relu_keep_nan(acc1[4 * q4 + 1]);
+      s1 = s1 + relu_keep_nan(acc1[4 * q4 + 2]);
+      s1 = s1 + relu_keep_nan(acc1[4 * q4 + 3]);
+      if (blk0 < ovis[q4]) orow[q4][blk0] = s0 * kScale;
+      if (blk0 + 32 < ovis[q4]) orow[q4][blk0 + 32] = s1 * kScale;
+    }
+    if (more) stash(buf ^ 1);
     __syncthreads();
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      const int col = ng * kNPerWave + ns * 32 + (lane & 31);
-      f32x16_t acc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t bfrag = *reinterpret_cast<const bf16x8_t*>(&bs[col][16 * ks + khalf]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], bfrag, acc, 0, 0, 0);
-      }
-      const int64_t blk = nb0 + col;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int lr = 8 * m + 2 * q4 + (lane >> 5);
-        float s = relu_keep_nan(acc[4 * q4 + 0]) + relu_keep_nan(acc[4 * q4 + 1]);
-        s = s + relu_keep_nan(acc[4 * q4 + 2]);
-        s = s + relu_keep_nan(acc[4 * q4 + 3]);
-        s = s * kScale;
-        if (blk < nvis[lr]) a.scores[(row0 + lr) * a.score_cols + blk] = s;
-      }
-    }
+    buf ^= 1;
   }
 }
 
@@ -248,7 +287,7 @@ hipError_t launch_score_wm(const ScoreArgs& base, hipStream_t stream) {
   // whose position is out of range even when no block is complete.
   int64_t n_tiles = (nb_total + S::TILE - 1) / S::TILE;
   if (n_tiles < 1) n_tiles = 1;
-  int64_t splits = (2048 + a.row_groups - 1) / a.row_groups;
+  int64_t splits = (1024 + a.row_groups - 1) / a.row_groups;
   if (splits < 1) splits = 1;
   if (splits > n_tiles) splits = n_tiles;
   a.tiles_per_split = (n_tiles + splits - 1) / splits;
