@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the QSA indexer hot path on one MI355X.
 
-One step = qsa_pool_keys (every block) -> qsa_score_rows (every row) ->
-qsa_select_mask (every row) over one batch of a seeded synthetic workload,
+One step = qsa_pool_keys (every block) -> qsa_prep_queries (every row) ->
+qsa_score_prepped (every row) -> qsa_select_mask (every row) over one batch
+of a seeded synthetic workload,
 inputs resident in HBM.  W untimed warm-up steps, then K timed steps between
 two device synchronisations; per-kernel durations come from HIP events
 recorded on the launch stream around each call.
@@ -61,6 +62,7 @@ class Device:
         self.wq = torch.from_numpy(w["q_norm_w"].view(np_.int16)).to(dev)
         self.pos = torch.from_numpy(w["pos"].astype(np_.int32)).to(dev)
         self.pooled = torch.empty((T // 4, 128), dtype=torch.int16, device=dev)
+        self.qhat = torch.empty((rows, 4, 128), dtype=torch.int16, device=dev)
         self.scores = torch.empty(rows * max(self.cols, 1), dtype=torch.float32, device=dev)
         self.mask = torch.empty((rows, T), dtype=torch.uint8, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -72,10 +74,14 @@ class Device:
         w = self.w
         self.qsa.qsa_pool_keys(self.raw, self.wk, w["rotary_dim"], w["theta"], w["eps"], self.pooled)
 
-    def score(self):
+    def prep(self):
         w = self.w
-        self.qsa.qsa_score_rows(self.q, self.pos, self.wq, w["rotary_dim"], w["theta"], w["eps"],
-                                self.pooled, self.T, self.scores, self.cols, self.status)
+        self.qsa.qsa_prep_queries(self.q, self.pos, self.wq, w["rotary_dim"], w["theta"], w["eps"],
+                                  self.T, self.qhat, self.status)
+
+    def score(self):
+        self.qsa.qsa_score_prepped(self.qhat, self.pos, self.pooled, self.T, self.scores, self.cols,
+                                   self.status)
 
     def select(self):
         self.qsa.qsa_select_mask(self.scores, self.cols, self.pos, self.T, self.w["budget"],
@@ -84,6 +90,9 @@ class Device:
     # algorithmic bytes / flops per launch
     def pool_bytes(self):
         return (self.T // 4) * (4 * 256 + 256)
+
+    def prep_bytes(self):
+        return self.rows * (1024 + 4 + 1024) + 256
 
     def score_bytes(self):
         return self.nmax * 256 + self.rows * (1024 + 4) + 4 * self.pairs
@@ -96,7 +105,7 @@ class Device:
 
 
 def time_steps(d: Device, steps: int, warmup: int, torch):
-    stages = (("pool", d.pool), ("score", d.score), ("select", d.select))
+    stages = (("pool", d.pool), ("prep", d.prep), ("score", d.score), ("select", d.select))
     for _ in range(warmup):
         for _, fn in stages:
             fn()
@@ -126,7 +135,8 @@ def median(xs):
 def kernel_report(d: Device, per_us):
     mean = {k: sum(v) / len(v) for k, v in per_us.items()}
     rep = {}
-    for name, b in (("pool", d.pool_bytes()), ("score", d.score_bytes()), ("select", d.select_bytes())):
+    for name, b in (("pool", d.pool_bytes()), ("prep", d.prep_bytes()), ("score", d.score_bytes()),
+                    ("select", d.select_bytes())):
         t = mean[name]
         gbs = b / (t * 1e-6) / 1e9
         rep[name] = {"mean_us": round(t, 3), "median_us": round(median(per_us[name]), 3),

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -113,6 +113,45 @@ int qsa_score_rows(const uint16_t* q, int64_t q_stride, const int32_t* pos, int6
                    float rms_eps, const uint16_t* pooled, int64_t tokens, float* scores,
                    int64_t score_cols, int64_t scores_len, int32_t* dev_status,
                    void* stream);
+
+/*
+ * qsa_prep_queries -- the normed, roped query heads of every row, computed
+ * once per row, for qsa_score_prepped.
+ *
+ * [SCORE] summary: each of the row's 4 query heads is (1 + w) RMSNorm-ed with
+ * q_norm_w and roped at the row's own position p, with the norm and rotary
+ * conventions of qsa_pool_keys.  Splitting this step out lets the scorer
+ * read finished query fragments instead of redoing the prep in every
+ * workgroup that scores a slice of the row's blocks.
+ *
+ *   q, pos, q_norm_w, rotary_dim, rope_theta, rms_eps, tokens: as for
+ *               qsa_score_rows (tokens bounds the valid positions).
+ *   qhat        [rows, 4, 128] bf16, dense (row stride 512 elements), written
+ *               for every row; a row with pos outside [0, tokens) is written
+ *               as zeros and sets QSA_STATUS_BAD_POSITION.
+ * Refusals: QSA_ERR_NULL, QSA_ERR_EXTENT (negative rows/tokens),
+ * QSA_ERR_STRIDE (q_stride < 512), QSA_ERR_CAPACITY (rows > INT32_MAX,
+ * tokens > QSA_MAX_TOKENS), QSA_ERR_PARAM.
+ */
+int qsa_prep_queries(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                     const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
+                     float rms_eps, int64_t tokens, uint16_t* qhat, int32_t* dev_status,
+                     void* stream);
+
+/*
+ * qsa_score_prepped -- qsa_score_rows on queries already prepared by
+ * qsa_prep_queries.  Same scores, bit for bit, as qsa_score_rows on the raw
+ * queries with the same norm and rotary arguments.
+ *
+ *   qhat        [rows, 4, 128] bf16 from qsa_prep_queries.
+ *   pos, pooled, tokens, scores, score_cols, scores_len, dev_status: as for
+ *               qsa_score_rows.
+ * Refusals: as for qsa_score_rows, without the rotary/norm parameters.
+ */
+int qsa_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                      const uint16_t* pooled, int64_t tokens, float* scores,
+                      int64_t score_cols, int64_t scores_len, int32_t* dev_status,
+                      void* stream);
 
 /*
  * qsa_select_mask -- exact per-row top-(budget/4) block select and the u8

@@ -17,7 +17,8 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
                    STATUS_BAD_POSITION, STATUS_NONFINITE_SCORE, QsaError, abi_version, load,
                    strerror)
 
-__all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_select_mask", "qsa_rope_inv_freq",
+__all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
+           "qsa_select_mask", "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
@@ -104,6 +105,52 @@ def qsa_score_rows(q: torch.Tensor, pos: torch.Tensor, q_norm_w: torch.Tensor, r
                               rope_theta, rms_eps, _ptr(pooled), tokens, _ptr(scores),
                               score_cols, scores.numel(), _ptr(dev_status), _stream_ptr(stream)),
            "qsa_score_rows")
+
+
+def qsa_prep_queries(q: torch.Tensor, pos: torch.Tensor, q_norm_w: torch.Tensor,
+                     rotary_dim: int, rope_theta: float, rms_eps: float, tokens: int,
+                     qhat: torch.Tensor, dev_status: torch.Tensor, stream=None) -> None:
+    """Normed, roped query heads of q [rows, >=512] at positions pos into
+    qhat [rows, 4, 128] (bf16 bits, contiguous)."""
+    _dev(q, "q", _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(q_norm_w, "q_norm_w", _BF16_LIKE)
+    _dev(qhat, "qhat", _BF16_LIKE)
+    _dev(dev_status, "dev_status", (torch.int32,))
+    q_stride = _rows_2d(q, "q", HEADS * HEAD_DIM)
+    rows = q.shape[0]
+    _need(pos.is_contiguous() and pos.numel() == rows, "pos must be contiguous [rows]")
+    _need(q_norm_w.numel() == HEAD_DIM and q_norm_w.is_contiguous(), "q_norm_w must hold 128 values")
+    _need(qhat.is_contiguous() and qhat.numel() >= rows * HEADS * HEAD_DIM,
+          "qhat must be contiguous [rows, 4, 128]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    lib = load()
+    _check(lib.qsa_prep_queries(_ptr(q), q_stride, _ptr(pos), rows, _ptr(q_norm_w), rotary_dim,
+                                rope_theta, rms_eps, tokens, _ptr(qhat), _ptr(dev_status),
+                                _stream_ptr(stream)), "qsa_prep_queries")
+
+
+def qsa_score_prepped(qhat: torch.Tensor, pos: torch.Tensor, pooled: torch.Tensor, tokens: int,
+                      scores: torch.Tensor, score_cols: int, dev_status: torch.Tensor,
+                      stream=None) -> None:
+    """qsa_score_rows on queries prepared by qsa_prep_queries."""
+    _dev(qhat, "qhat", _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(pooled, "pooled", _BF16_LIKE)
+    _dev(scores, "scores", (torch.float32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous(), "pos must be contiguous")
+    _need(qhat.is_contiguous() and qhat.numel() >= rows * HEADS * HEAD_DIM,
+          "qhat must be contiguous [rows, 4, 128]")
+    _need(pooled.is_contiguous() and pooled.numel() >= (tokens // RATIO) * HEAD_DIM,
+          "pooled must be contiguous and cover tokens/4 blocks")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    lib = load()
+    _check(lib.qsa_score_prepped(_ptr(qhat), _ptr(pos), rows, _ptr(pooled), tokens, _ptr(scores),
+                                 score_cols, scores.numel(), _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_score_prepped")
 
 
 def qsa_select_mask(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, tokens: int,

@@ -30,8 +30,9 @@ MAX_KEEP_BLOCKS = 512
 MAX_TOKENS = 262147
 
 # Every symbol the header declares.
-EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_select_mask", "qsa_rope_inv_freq",
-           "qsa_strerror", "qsa_abi_version")
+EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
+           "qsa_select_mask", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
+ABI_VERSION = 2
 
 _lib = None
 
@@ -56,6 +57,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_pool_keys.restype = ctypes.c_int
     lib.qsa_score_rows.argtypes = [P, I64, P, I64, P, I32, F, F, P, I64, P, I64, I64, P, P]
     lib.qsa_score_rows.restype = ctypes.c_int
+    lib.qsa_prep_queries.argtypes = [P, I64, P, I64, P, I32, F, F, I64, P, P, P]
+    lib.qsa_prep_queries.restype = ctypes.c_int
+    lib.qsa_score_prepped.argtypes = [P, P, I64, P, I64, P, I64, I64, P, P]
+    lib.qsa_score_prepped.restype = ctypes.c_int
     lib.qsa_select_mask.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P]
     lib.qsa_select_mask.restype = ctypes.c_int
     lib.qsa_rope_inv_freq.argtypes = [I32, F, P]

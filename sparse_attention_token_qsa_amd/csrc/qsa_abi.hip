@@ -105,6 +105,48 @@ int qsa_score_rows(const uint16_t* q, int64_t q_stride, const int32_t* pos, int6
                                          static_cast<hipStream_t>(stream)));
 }
 
+int qsa_prep_queries(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                     const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
+                     float rms_eps, int64_t tokens, uint16_t* qhat, int32_t* dev_status,
+                     void* stream) {
+  if (rows < 0 || tokens < 0) return QSA_ERR_EXTENT;
+  if (q_stride < QSA_HEADS * QSA_HEAD_DIM) return QSA_ERR_STRIDE;
+  const int rc = check_rope(rotary_dim, rope_theta, rms_eps);
+  if (rc != QSA_OK) return rc;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0) return QSA_OK;
+  if (q == nullptr || pos == nullptr || q_norm_w == nullptr || qhat == nullptr ||
+      dev_status == nullptr)
+    return QSA_ERR_NULL;
+  int64_t need;
+  if (mul_overflows(rows, q_stride, &need)) return QSA_ERR_CAPACITY;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_prep(q, q_stride, pos, rows, q_norm_w, rp, tokens, qhat,
+                                        dev_status, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                      const uint16_t* pooled, int64_t tokens, float* scores,
+                      int64_t score_cols, int64_t scores_len, int32_t* dev_status,
+                      void* stream) {
+  if (rows < 0 || tokens < 0 || score_cols < 0 || scores_len < 0) return QSA_ERR_EXTENT;
+  if (score_cols < tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0 || tokens == 0) return QSA_OK;
+  if (qhat == nullptr || pos == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
+  if (tokens >= QSA_RATIO && (pooled == nullptr || scores == nullptr)) return QSA_ERR_NULL;
+  return launch_status(qsa::launch_score_prepped(qhat, pos, rows, pooled, tokens, scores,
+                                                 score_cols, dev_status,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
                     const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
                     uint8_t* mask, int32_t* dev_status, void* stream) {

@@ -26,6 +26,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 // Round a float to the nearest bf16 value, returned as float.
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// f32 rounded to the nearest bf16 value by the hardware conversion
+// (v_cvt_pk_bf16_f32: round to nearest even, like f32_to_bf16 on every
+// non-NaN input; a NaN stays a NaN but keeps its sign and payload).
+__device__ __forceinline__ float rb_hw(float f) { return static_cast<float>(static_cast<__bf16>(f)); }
+
+// Two floats to packed bf16 (lo in bits 0..15) by the hardware conversion,
+// with every NaN written as the canonical 0x7FC0.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if (lo != lo) u = (u & 0xFFFF0000u) | 0x7FC0u;
+  if (hi != hi) u = (u & 0x0000FFFFu) | 0x7FC00000u;
+  return u;
+}
+
 // Order-preserving map of a finite float to u32: a larger score gives a
 // larger key; -0.0 is folded onto +0.0 so the two zeros tie.
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -22,6 +22,14 @@ hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos,
                         int64_t tokens, float* scores, int64_t score_cols, int32_t* status,
                         hipStream_t stream);
 
+hipError_t launch_prep(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                       const uint16_t* w, const RopeParams& rp, int64_t tokens, uint16_t* qhat,
+                       int32_t* status, hipStream_t stream);
+
+hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                                const uint16_t* pooled, int64_t tokens, float* scores,
+                                int64_t score_cols, int32_t* status, hipStream_t stream);
+
 hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t* pos,
                          int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                          int32_t* status, hipStream_t stream);

@@ -30,11 +30,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kScoreThreads = 256;
-constexpr int kNPerWave = 64;  // two 32-block MFMA tiles per wave and iteration
-constexpr int kPitch = 136;    // LDS row pitch in bf16 elements (272 bytes)
+constexpr int kPitch = 136;  // LDS row pitch in bf16 elements (272 bytes)
 constexpr float kScale = static_cast<float>(0.088388347648318440550);  // 1/sqrt(128)
 
 struct ScoreArgs {
+  const uint16_t* qhat;  // prepared queries [rows, 4, 128] bf16 (PREP kernels)
   const uint16_t* q;
   int64_t q_stride;
   const int32_t* pos;
@@ -47,255 +47,407 @@ struct ScoreArgs {
   int32_t* status;
   int64_t tiles_per_split;
   int64_t row_groups;
+  int64_t tasks;
   int q_vec;
-  int pooled_vec;
+  int pooled_vec;  // pooled keys 16-byte aligned (host-side choice of kernel)
   RopeParams rp;
 };
 
 __device__ __forceinline__ float relu_keep_nan(float x) { return x < 0.0f ? 0.0f : x; }
 
-template <int WM>
-struct ScoreSmem {
+// Sum over the 16 lanes of a DPP row, returned in all 16 (rotations 8, 4, 2,
+// 1).  Used on sums of squares of bf16 values, which are exact in double in
+// any order, so every lane gets the same value.
+__device__ __forceinline__ double row16_sum(double v) {
+#define QSA_ROR_STEP(CTRL)                                                                  \
+  {                                                                                         \
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false); \
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false); \
+    v += __hiloint2double(hi, lo);                                                          \
+  }
+  QSA_ROR_STEP(0x128)  // row_ror 8
+  QSA_ROR_STEP(0x124)  // row_ror 4
+  QSA_ROR_STEP(0x122)  // row_ror 2
+  QSA_ROR_STEP(0x121)  // row_ror 1
+#undef QSA_ROR_STEP
+  return v;
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
+  uint4 o;
+  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+  o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+  return o;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 u, float (&v)[8]) {
+  const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(wd[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(wd[i] >> 16);
+  }
+}
+
+// Workgroup geometry.  WM waves along M (8 query rows = 32 M-rows each),
+// WN = 4 / WM waves along N, NS 32-block MFMA tiles per wave and step.
+template <int WM, int NS>
+struct ScoreGeom {
   static constexpr int WN = 4 / WM;
-  static constexpr int RG = 8 * WM;           // query rows per workgroup
-  static constexpr int TILE = kNPerWave * WN;  // blocks per iteration
-  // prologue: normed + roped queries, the norm's partner buffer, cos/sin
+  static constexpr int RG = 8 * WM;            // query rows per workgroup
+  static constexpr int TILE = 32 * NS * WN;    // blocks per step
+  static constexpr int NPASS = RG * 4 / 16;    // head vectors per 16-lane group
+  static constexpr int kChunks = TILE * 16 / kScoreThreads;  // 16-byte loads per thread per tile
+  // prologue: normed + roped queries, then packed bf16 (cos, sin) per row and frequency
   static constexpr int kQBytes = RG * 4 * kPitch * 2;
-  static constexpr int kPrologueBytes = kQBytes + 16 * kHeadDim * 4 + RG * kMaxHalfRotary * 8;
+  static constexpr int kPrologueBytes = kQBytes + RG * kMaxHalfRotary * 4;
   // block loop: two key tiles
   static constexpr int kTileBytes = TILE * kPitch * 2;
   static constexpr int kBytes = kPrologueBytes > 2 * kTileBytes ? kPrologueBytes : 2 * kTileBytes;
-  static constexpr int kChunks = TILE * 16 / kScoreThreads;  // 16-byte loads per thread per tile
 };
 
-template <int WM>
+template <int WM, int NS, bool VECP, bool BUFST, bool PREP>
 __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreArgs a) {
-  using S = ScoreSmem<WM>;
-  constexpr int RG = S::RG;
-  constexpr int TILE = S::TILE;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
+  using G = ScoreGeom<WM, NS>;
+  constexpr int RG = G::RG;
+  constexpr int TILE = G::TILE;
+  constexpr int NPASS = G::NPASS;
+  constexpr int KC = G::kChunks;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PREP ? 2 * G::kTileBytes : G::kBytes];
   __shared__ int nvis[RG];
   __shared__ int ppos[RG];
   __shared__ int sh_nmax;
 
   uint16_t(*qs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem);
-  float(*ybuf)[kHeadDim] = reinterpret_cast<float(*)[kHeadDim]>(smem + S::kQBytes);
-  float2(*csq)[kMaxHalfRotary] =
-      reinterpret_cast<float2(*)[kMaxHalfRotary]>(smem + S::kQBytes + 16 * kHeadDim * 4);
+  uint32_t(*csq)[kMaxHalfRotary] = reinterpret_cast<uint32_t(*)[kMaxHalfRotary]>(smem + G::kQBytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t rg = static_cast<int64_t>(blockIdx.x) % a.row_groups;
-  const int64_t split = static_cast<int64_t>(blockIdx.x) / a.row_groups;
+
+  // Task order: tasks that share a block range are kept on one XCD (the
+  // hardware deals consecutive workgroups round-robin over 8 XCDs), so each
+  // XCD's L2 holds only its share of the pooled keys.
+  int64_t task = blockIdx.x;
+  {
+    const int64_t per = a.tasks >> 3;
+    if (task < (per << 3)) task = (task & 7) * per + (task >> 3);
+  }
+  const int64_t rg = task % a.row_groups;
+  const int64_t split = task / a.row_groups;
   const int64_t row0 = rg * RG;
+  const int nb_total = static_cast<int>(a.tokens / kRatio);
+  const int blk_begin = static_cast<int>(split * a.tiles_per_split * TILE);
+  const int blk_stop = static_cast<int>(min((split + 1) * a.tiles_per_split * TILE, static_cast<int64_t>(nb_total)));
 
-  if (tid < RG) {
-    const int64_t r = row0 + tid;
-    int n = 0, p = 0;
-    if (r < a.rows) {
-      p = a.pos[r];
-      if (p >= 0 && p < a.tokens)
-        n = (p + 1) / kRatio;
-      else if (split == 0)
-        atomicOr(a.status, 1);
-    }
-    nvis[tid] = n;
-    ppos[tid] = p;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int mx = 0;
-    for (int i = 0; i < RG; ++i) mx = nvis[i] > mx ? nvis[i] : mx;
-    sh_nmax = mx;
-  }
-  __syncthreads();
-  const int64_t nmax = sh_nmax;
-  const int64_t blk_begin = split * a.tiles_per_split * TILE;
-  if (blk_begin >= nmax) return;  // uniform across the workgroup
-  int64_t blk_end = (split + 1) * a.tiles_per_split * TILE;
-  if (blk_end > nmax) blk_end = nmax;
-
-  // ---- key tiles: this thread's 16-byte chunks of a tile, loaded to
-  // registers one tile ahead of the MFMAs that read them from LDS.
-  uint4 pre[S::kChunks];
-  auto fetch = [&](int64_t nb0) {
+  // ---- key tiles: 16-byte chunks of a tile, held in registers from their
+  // load until they are written to LDS.  Block indices are clamped to the
+  // last block the workgroup may use, so loads never leave the cache and
+  // every step issues the same loads; blocks past the end are never stored.
+  auto fetch = [&](uint4 (&dst)[KC], int nb0, int last) {
 #pragma unroll
-    for (int i = 0; i < S::kChunks; ++i) {
+    for (int i = 0; i < KC; ++i) {
       const int idx = tid + i * kScoreThreads;
-      const int64_t bb = nb0 + (idx >> 4);
-      const int c = idx & 15;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (bb < blk_end) {
-        const uint16_t* src = a.pooled + bb * kHeadDim + 8 * c;
-        if (a.pooled_vec) {
-          v = *reinterpret_cast<const uint4*>(src);
-        } else {
-          v.x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
-          v.y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
-          v.z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
-          v.w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
-        }
+      int bb = nb0 + (idx >> 4);
+      bb = bb < last ? bb : last;
+      const uint16_t* src = a.pooled + static_cast<int64_t>(bb) * kHeadDim + 8 * (idx & 15);
+      if constexpr (VECP) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        dst[i].x = v.x;
+        dst[i].y = v.y;
+        dst[i].z = v.z;
+        dst[i].w = v.w;
+      } else {
+        dst[i].x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
+        dst[i].y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
+        dst[i].z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
+        dst[i].w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
       }
-      pre[i] = v;
     }
   };
-  auto stash = [&](int buf) {
-    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * S::kTileBytes);
+  auto stash = [&](const uint4 (&src)[KC], int buf) {
+    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * G::kTileBytes);
 #pragma unroll
-    for (int i = 0; i < S::kChunks; ++i) {
+    for (int i = 0; i < KC; ++i) {
       const int idx = tid + i * kScoreThreads;
-      *reinterpret_cast<uint4*>(&bs[idx >> 4][8 * (idx & 15)]) = pre[i];
+      *reinterpret_cast<uint4*>(&bs[idx >> 4][8 * (idx & 15)]) = src[i];
     }
   };
-  fetch(blk_begin);  // in flight during the query prep
-
-  // ---- query prep: (1 + w) RMSNorm per head, then RoPE at the row's position.
-  const int rd = a.rp.rotary_dim;
-  const int half = rd >> 1;
-  for (int idx = tid; idx < RG * half; idx += kScoreThreads) {
-    const int r = idx / half;
-    const int i = idx - r * half;
-    float c, s;
-    rope_cos_sin(ppos[r], a.rp.inv_freq[i], c, s);
-    csq[r][i] = make_float2(c, s);
+  uint4 pa[KC], pb[KC];
+  if (blk_begin < blk_stop) {
+    fetch(pa, blk_begin, blk_stop - 1);
+    fetch(pb, blk_begin + TILE, blk_stop - 1);
   }
-  const int hv_local = tid >> 4;  // head vector handled by this 16-lane group
+
+  // ---- query loads: 16-lane group `hv_local` takes head vector
+  // pass * 16 + hv_local (= 4 * local_row + head), 8 channels per lane.
+  // Prepared queries are loaded straight into A fragments instead.
+  const int m = wave % WM;
+  const int ng = wave / WM;
+  const int khalf = 8 * (lane >> 5);
+  bf16x8_t afrag[8];
+  if constexpr (PREP) {
+    int64_t rr = row0 + ((32 * m + (lane & 31)) >> 2);
+    rr = rr < a.rows ? rr : a.rows - 1;  // rows past the end are never stored
+    const uint16_t* src = a.qhat + rr * (kHeads * kHeadDim) + kHeadDim * (lane & 3) + khalf;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) afrag[ks] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ks);
+  }
+  const int hv_local = tid >> 4;
   const int g = tid & 15;
+  uint4 xq[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int hv = p * 16 + hv_local;
+    const int64_t r = row0 + (hv >> 2);
+    xq[p] = make_uint4(0u, 0u, 0u, 0u);
+    if (!PREP && r < a.rows) {
+      const uint16_t* src = a.q + r * a.q_stride + kHeadDim * (hv & 3) + 8 * g;
+      if (a.q_vec) {
+        xq[p] = *reinterpret_cast<const uint4*>(src);
+      } else {
+        xq[p].x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
+        xq[p].y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
+        xq[p].z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
+        xq[p].w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
+      }
+    }
+  }
   float wv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) wv[e] = bf16_to_f32(a.w[8 * g + e]);
-  for (int pass = 0; pass < RG * 4 / 16; ++pass) {
-    const int hv = pass * 16 + hv_local;  // = 4 * local_row + head
-    const int lr = hv >> 2;
-    const int h = hv & 3;
-    float x[8];
-    if (row0 + lr < a.rows && ppos[lr] >= 0 && ppos[lr] < a.tokens) {
-      const uint16_t* src = a.q + (row0 + lr) * a.q_stride + kHeadDim * h + 8 * g;
-      if (a.q_vec) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[2 * i] = bf16_to_f32(wd[i] & 0xFFFFu);
-          x[2 * i + 1] = bf16_to_f32(wd[i] >> 16);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(src[e]);
+  for (int e = 0; e < 8; ++e) wv[e] = PREP ? 0.0f : bf16_to_f32(a.w[8 * g + e]);
+
+  // ---- positions and visible block counts (wave 0)
+  if (wave == 0) {
+    int n = 0, p = 0;
+    if (lane < RG) {
+      const int64_t r = row0 + lane;
+      if (r < a.rows) {
+        p = a.pos[r];
+        if (p >= 0 && p < a.tokens)
+          n = (p + 1) / kRatio;
+        else if (split == 0)
+          atomicOr(a.status, 1);
       }
-    } else {
+      nvis[lane] = n;
+      ppos[lane] = p;
+    }
+    const uint32_t mx = wave_max_u32(static_cast<uint32_t>(n));
+    if (lane == 0) sh_nmax = static_cast<int>(mx);
+  }
+  __syncthreads();
+  const int nmax = sh_nmax;
+  if (blk_begin >= nmax) return;  // uniform across the workgroup
+  const int blk_end = blk_stop < nmax ? blk_stop : nmax;
+
+  if constexpr (!PREP) {
+  // ---- cos/sin of every (row, frequency), four per thread in flight
+  const int rd = a.rp.rotary_dim;
+  const int half = rd >> 1;
+  const int ncs = RG * half;
+  for (int base = 0; base < ncs; base += 4 * kScoreThreads) {
+    float cv[4], sv[4];
+    int ri[4], fi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int idx = base + u * kScoreThreads + tid;
+      idx = idx < ncs ? idx : ncs - 1;
+      ri[u] = idx / half;
+      fi[u] = idx - ri[u] * half;
+      rope_cos_sin(ppos[ri[u]], a.rp.inv_freq[fi[u]], cv[u], sv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (base + u * kScoreThreads + tid < ncs)
+        csq[ri[u]][fi[u]] = f32_to_bf16(cv[u]) | (f32_to_bf16(sv[u]) << 16);
+  }
+
+  // ---- (1 + w) RMSNorm of every head vector this group holds
+  float y[NPASS][8];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int lr = (p * 16 + hv_local) >> 2;
+    float x[8];
+    unpack_bf16x8(xq[p], x);
+    if (!(ppos[lr] >= 0 && ppos[lr] < a.tokens)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.0f;
     }
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += static_cast<double>(x[e]) * static_cast<double>(x[e]);
+    const double rinv = inv_rms(row16_sum(ss), a.rp.eps);
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    const double rinv = inv_rms(ss, a.rp.eps);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[e] = norm_channel(x[e], rinv, wv[e]);
-      ybuf[hv_local][8 * g + e] = y[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 8 * g + e;
-      float o = y[e];
-      if (c < rd) {
-        const bool first = c < half;
-        const float xp = ybuf[hv_local][first ? c + half : c - half];
-        const float2 cs = csq[lr][first ? c : c - half];
-        o = rope_channel(y[e], xp, cs.x, cs.y, first);
-      }
-      qs[hv][8 * g + e] = static_cast<uint16_t>(f32_to_bf16(o));
-    }
-    __syncthreads();
+    for (int e = 0; e < 8; ++e) y[p][e] = norm_channel(x[e], rinv, wv[e]);
   }
+  __syncthreads();  // cos/sin table complete
+  // ---- RoPE at the row's position.  The group's own row of qs is the
+  // exchange buffer: normed values go in, partners are read back, the roped
+  // values replace them.  A group lives in one wave, so wave-level ordering
+  // of LDS traffic is enough here.
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p)
+    *reinterpret_cast<uint4*>(&qs[p * 16 + hv_local][8 * g]) = pack_bf16x8(y[p]);
+  wave_lds_sync();
+  uint4 outq[NPASS];
+  const bool fast = (half & 7) == 0;  // chunks of 8 never straddle the halves
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int hv = p * 16 + hv_local;
+    const int lr = hv >> 2;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = y[p][e];
+    if (fast) {
+      const int c0 = 8 * g;
+      if (c0 < rd) {
+        const bool first = c0 < half;
+        float xp[8];
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(&qs[hv][first ? c0 + half : c0 - half]), xp);
+        const int f0 = first ? c0 : c0 - half;
+        const uint4 cs0 = *reinterpret_cast<const uint4*>(&csq[lr][f0]);
+        const uint4 cs1 = *reinterpret_cast<const uint4*>(&csq[lr][f0 + 4]);
+        const uint32_t cs[8] = {cs0.x, cs0.y, cs0.z, cs0.w, cs1.x, cs1.y, cs1.z, cs1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = rope_channel(y[p][e], xp[e], bf16_to_f32(cs[e] & 0xFFFFu), bf16_to_f32(cs[e] >> 16), first);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * g + e;
+        if (c < rd) {
+          const bool first = c < half;
+          const float xp = bf16_to_f32(qs[hv][first ? c + half : c - half]);
+          const uint32_t cs = csq[lr][first ? c : c - half];
+          o[e] = rope_channel(y[p][e], xp, bf16_to_f32(cs & 0xFFFFu), bf16_to_f32(cs >> 16), first);
+        }
+      }
+    }
+    outq[p] = pack_bf16x8(o);
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) *reinterpret_cast<uint4*>(&qs[p * 16 + hv_local][8 * g]) = outq[p];
+  __syncthreads();
 
   // ---- A fragments: this wave's 32 M-rows (8 query rows x 4 heads), K = 128.
-  const int m = wave % WM;
-  const int ng = wave / WM;
-  const int mrow = 32 * m + (lane & 31);
-  const int khalf = 8 * (lane >> 5);
-  bf16x8_t afrag[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
-    afrag[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[mrow][16 * ks + khalf]);
+    afrag[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[32 * m + (lane & 31)][16 * ks + khalf]);
 
-  // per-lane output rows: this lane holds rows 8m + 2 q4 + (lane >> 5)
+  }
+
+  // per-lane output rows: this lane holds rows 8m + 2 q4 + (lane >> 5).
+  // With BUFST the stores go through a buffer resource over the workgroup's
+  // rows: a lane whose block is past its row's prefix gets an offset past
+  // the resource's end, and the hardware drops that store.  The stores then
+  // carry no branch, so the loads issued after them never wait behind them.
   float* orow[4];
   int ovis[4];
+  int ooff[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int lr = 8 * m + 2 * q4 + (lane >> 5);
     orow[q4] = a.scores + (row0 + lr) * a.score_cols;
     ovis[q4] = nvis[lr];
+    ooff[q4] = lr * static_cast<int>(a.score_cols) * 4;
   }
-  __syncthreads();  // every wave holds its A fragments: the LDS becomes key tiles
-  stash(0);
+  __amdgpu_buffer_rsrc_t out_rsrc;
+  if constexpr (BUFST)
+    out_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.scores + row0 * a.score_cols, static_cast<short>(0),
+                                                 static_cast<int>(RG * a.score_cols * 4), 0x00020000);
+  if constexpr (!PREP) __syncthreads();  // every wave holds its A fragments: the LDS becomes key tiles
+  stash(pa, 0);
   __syncthreads();
 
-  // ---- block loop: MFMAs on tile t (LDS) while tile t+1 is fetched
-  int buf = 0;
-  for (int64_t nb0 = blk_begin; nb0 < blk_end; nb0 += TILE) {
-    const bool more = nb0 + TILE < blk_end;
-    if (more) fetch(nb0 + TILE);
-    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * S::kTileBytes);
-    const int col0 = ng * kNPerWave + (lane & 31);
-    f32x16_t acc0, acc1;
+  // ---- block loop.  Step t: LDS buffer t&1 holds tile t, one register set
+  // holds tile t+1; tile t+2 is loaded into the other set, the MFMAs run on
+  // tile t, tile t+1 goes to LDS, then tile t's scores are stored.  Loads are
+  // issued before the stores they must not wait behind.
+  const int col0 = ng * (32 * NS) + (lane & 31);
+  auto step = [&](int nb0, int buf, uint4 (&ld)[KC], uint4 (&st)[KC]) {
+    fetch(ld, nb0 + 2 * TILE, blk_end - 1);
+    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * G::kTileBytes);
+    f32x16_t acc[NS];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      acc0[v] = 0.0f;
-      acc1[v] = 0.0f;
-    }
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[n][v] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&bs[col0][16 * ks + khalf]);
-      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&bs[col0 + 32][16 * ks + khalf]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], b1, acc1, 0, 0, 0);
-    }
-    const int blk0 = static_cast<int>(nb0) + col0;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float s0 = relu_keep_nan(acc0[4 * q4 + 0]) + relu_keep_nan(acc0[4 * q4 + 1]);
-      s0 = s0 + relu_keep_nan(acc0[4 * q4 + 2]);
-      s0 = s0 + relu_keep_nan(acc0[4 * q4 + 3]);
-      float s1 = relu_keep_nan(acc1[4 * q4 + 0]) + relu_keep_nan(acc1[4 * q4 + 1]);
-      s1 = s1 + relu_keep_nan(acc1[4 * q4 + 2]);
-      s1 = s1 + relu_keep_nan(acc1[4 * q4 + 3]);
-      if (blk0 < ovis[q4]) orow[q4][blk0] = s0 * kScale;
-      if (blk0 + 32 < ovis[q4]) orow[q4][blk0 + 32] = s1 * kScale;
+      for (int n = 0; n < NS; ++n) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&bs[col0 + 32 * n][16 * ks + khalf]);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], b, acc[n], 0, 0, 0);
+      }
     }
-    if (more) stash(buf ^ 1);
+    stash(st, buf ^ 1);
+    const int blk0 = nb0 + col0;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      const int blk = blk0 + 32 * n;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float s = relu_keep_nan(acc[n][4 * q4 + 0]) + relu_keep_nan(acc[n][4 * q4 + 1]);
+        s = s + relu_keep_nan(acc[n][4 * q4 + 2]);
+        s = s + relu_keep_nan(acc[n][4 * q4 + 3]);
+        if constexpr (BUFST) {
+          const int off = blk < ovis[q4] ? ooff[q4] + 4 * blk : static_cast<int>(0x80000000u);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * kScale), out_rsrc, off, 0, 0);
+        } else {
+          if (blk < ovis[q4]) orow[q4][blk] = s * kScale;
+        }
+      }
+    }
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int nb0 = blk_begin; nb0 < blk_end; nb0 += 2 * TILE) {
+    step(nb0, 0, pa, pb);
+    if (nb0 + TILE >= blk_end) break;
+    step(nb0 + TILE, 1, pb, pa);
   }
 }
 
-template <int WM>
-hipError_t launch_score_wm(const ScoreArgs& base, hipStream_t stream) {
-  using S = ScoreSmem<WM>;
+template <int WM, int NS, bool PREP>
+hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
+  using G = ScoreGeom<WM, NS>;
   ScoreArgs a = base;
   const int64_t nb_total = a.tokens / kRatio;
-  a.row_groups = (a.rows + S::RG - 1) / S::RG;
+  a.row_groups = (a.rows + G::RG - 1) / G::RG;
   // At least one tile: a workgroup per row group still runs, to flag rows
   // whose position is out of range even when no block is complete.
-  int64_t n_tiles = (nb_total + S::TILE - 1) / S::TILE;
+  int64_t n_tiles = (nb_total + G::TILE - 1) / G::TILE;
   if (n_tiles < 1) n_tiles = 1;
   int64_t splits = (1024 + a.row_groups - 1) / a.row_groups;
   if (splits < 1) splits = 1;
   if (splits > n_tiles) splits = n_tiles;
   a.tiles_per_split = (n_tiles + splits - 1) / splits;
   splits = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  const int64_t grid = a.row_groups * splits;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  score_mfma_kernel<WM><<<dim3(static_cast<unsigned>(grid)), dim3(kScoreThreads), 0, stream>>>(a);
+  a.tasks = a.row_groups * splits;
+  if (a.tasks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.tasks));
+  const dim3 block(kScoreThreads);
+  // buffer-resource stores need the workgroup's rows within 2^31 bytes
+  const bool bufst = a.score_cols <= 0x7FFFFFFF / (4 * G::RG);
+  if (a.pooled_vec && bufst)
+    score_mfma_kernel<WM, NS, true, true, PREP><<<grid, block, 0, stream>>>(a);
+  else if (a.pooled_vec)
+    score_mfma_kernel<WM, NS, true, false, PREP><<<grid, block, 0, stream>>>(a);
+  else if (bufst)
+    score_mfma_kernel<WM, NS, false, true, PREP><<<grid, block, 0, stream>>>(a);
+  else
+    score_mfma_kernel<WM, NS, false, false, PREP><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool PREP>
+hipError_t launch_score_rows(const ScoreArgs& a, hipStream_t stream) {
+  if (a.rows >= 32) return launch_score_geom<4, 2, PREP>(a, stream);
+  if (a.rows > 8) return launch_score_geom<2, 2, PREP>(a, stream);
+  return launch_score_geom<1, 1, PREP>(a, stream);
 }
 
 }  // namespace
@@ -318,9 +470,23 @@ hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos,
   a.q_vec = (q_stride % 8 == 0) && (reinterpret_cast<uintptr_t>(q) % 16 == 0);
   a.pooled_vec = reinterpret_cast<uintptr_t>(pooled) % 16 == 0;
   a.rp = rp;
-  if (rows >= 32) return launch_score_wm<4>(a, stream);
-  if (rows > 8) return launch_score_wm<2>(a, stream);
-  return launch_score_wm<1>(a, stream);
+  return launch_score_rows<false>(a, stream);
+}
+
+hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                                const uint16_t* pooled, int64_t tokens, float* scores,
+                                int64_t score_cols, int32_t* status, hipStream_t stream) {
+  ScoreArgs a{};
+  a.qhat = qhat;
+  a.pos = pos;
+  a.rows = rows;
+  a.pooled = pooled;
+  a.tokens = tokens;
+  a.scores = scores;
+  a.score_cols = score_cols;
+  a.status = status;
+  a.pooled_vec = reinterpret_cast<uintptr_t>(pooled) % 16 == 0;
+  return launch_score_rows<true>(a, stream);
 }
 
 }  // namespace qsa

@@ -72,6 +72,35 @@ def gpu_scores(w, pooled_dev, pos=None, q=None, score_cols=None, sentinel=np.flo
     return scores.cpu().numpy().reshape(rows, max(cols, 1)), s
 
 
+def gpu_prep(w, pos=None, q=None):
+    """Prepared queries [rows, 4, 128] (bf16 bits, read back) and status."""
+    T = w["tokens"]
+    pos = w["pos"] if pos is None else pos
+    q = w["queries"] if q is None else q
+    rows = len(pos)
+    qhat = torch.full((rows, 4, 128), 0x5A5A, dtype=torch.int16, device=DEV)
+    st = status_word()
+    qsa.qsa_prep_queries(u16_dev(q.reshape(rows, 512)), i32_dev(pos), u16_dev(w["q_norm_w"]),
+                         w["rotary_dim"], w["theta"], w["eps"], T, qhat, st)
+    s = qsa.check_status(st)
+    return qhat, s
+
+
+def gpu_scores_prepped(w, pooled_dev, pos=None, q=None, score_cols=None,
+                       sentinel=np.float32(-7.25)):
+    """gpu_scores through qsa_prep_queries + qsa_score_prepped."""
+    T = w["tokens"]
+    pos = w["pos"] if pos is None else pos
+    rows = len(pos)
+    cols = T // 4 if score_cols is None else score_cols
+    qhat, s1 = gpu_prep(w, pos=pos, q=q)
+    scores = torch.full((rows * max(cols, 1),), float(sentinel), dtype=torch.float32, device=DEV)
+    st = status_word()
+    qsa.qsa_score_prepped(qhat, i32_dev(pos), pooled_dev, T, scores, cols, st)
+    s2 = qsa.check_status(st)
+    return scores.cpu().numpy().reshape(rows, max(cols, 1)), s1 | s2
+
+
 def gpu_select(scores: np.ndarray, cols: int, pos, tokens: int, budget: int):
     rows = len(pos)
     mask = torch.full((rows, tokens), 0xAB, dtype=torch.uint8, device=DEV)

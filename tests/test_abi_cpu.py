@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 2
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -148,3 +148,47 @@ def test_select_refusals(lib):
     assert select(lib, scores_len=127) == CAP
     assert select(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
     assert select(lib, rows=2**40, score_cols=16, scores_len=2**62) == CAP
+
+
+def prep(lib, **kw):
+    a = dict(q=P, q_stride=512, pos=P, rows=8, w=P, rd=64, theta=1e4, eps=1e-6, tokens=64,
+             qhat=P, status=P)
+    a.update(kw)
+    return lib.qsa_prep_queries(a["q"], a["q_stride"], a["pos"], a["rows"], a["w"], a["rd"],
+                                a["theta"], a["eps"], a["tokens"], a["qhat"], a["status"], None)
+
+
+def test_prep_refusals(lib):
+    assert prep(lib, rows=0) == OK
+    for k in ("q", "pos", "w", "qhat", "status"):
+        assert prep(lib, **{k: None}) == NULL, k
+    assert prep(lib, rows=-1) == EXTENT
+    assert prep(lib, tokens=-1) == EXTENT
+    assert prep(lib, q_stride=500) == STRIDE
+    assert prep(lib, tokens=262148) == CAP
+    assert prep(lib, rows=2**31) == CAP
+    assert prep(lib, rows=2**40, q_stride=2**40) == CAP
+    assert prep(lib, rd=3) == PARAM
+    assert prep(lib, theta=float("inf")) == PARAM
+    assert prep(lib, eps=-0.5) == PARAM
+
+
+def score_prepped(lib, **kw):
+    a = dict(qhat=P, pos=P, rows=8, pooled=P, tokens=64, scores=P, score_cols=16, scores_len=128,
+             status=P)
+    a.update(kw)
+    return lib.qsa_score_prepped(a["qhat"], a["pos"], a["rows"], a["pooled"], a["tokens"],
+                                 a["scores"], a["score_cols"], a["scores_len"], a["status"], None)
+
+
+def test_score_prepped_refusals(lib):
+    assert score_prepped(lib, rows=0) == OK
+    assert score_prepped(lib, tokens=0, score_cols=0) == OK
+    for k in ("qhat", "pos", "pooled", "scores", "status"):
+        assert score_prepped(lib, **{k: None}) == NULL, k
+    assert score_prepped(lib, rows=-1) == EXTENT
+    assert score_prepped(lib, scores_len=-1) == EXTENT
+    assert score_prepped(lib, score_cols=15) == STRIDE
+    assert score_prepped(lib, scores_len=127) == CAP
+    assert score_prepped(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
+    assert score_prepped(lib, rows=2**40, scores_len=2**62, score_cols=2**20) == CAP

@@ -14,8 +14,8 @@ import torch
 
 import oracle as O
 import synth
-from tests.gpu_util import (DEV, gpu_pool, gpu_scores, gpu_select, note, u16_dev, u16_host,
-                            workload)
+from tests.gpu_util import (DEV, gpu_pool, gpu_prep, gpu_scores, gpu_scores_prepped, gpu_select,
+                            note, u16_dev, u16_host, workload)
 from tests.test_oracle_pins import check_structure
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +45,14 @@ def oracle_scores(wid, rows):
     qhat = O.prep_queries(w["queries"][rows], w["pos"][rows], w["q_norm_w"], w["rotary_dim"],
                           w["theta"], w["eps"])
     return O.score_rows(qhat, w["pos"][rows], oracle_pooled(wid), w["tokens"])
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_sample_scores(wid):
+    return oracle_scores(wid, sample_rows(wid))
+
+
+SCORERS = {"fused": gpu_scores, "prepped": gpu_scores_prepped}
 
 
 def dense(score_list, cols):
@@ -94,6 +102,53 @@ def test_pool_nan_key_poisons_only_its_block():
     got = O.f32_from_bf16(u16_host(gpu_pool(w)))
     assert np.all(np.isnan(got[50]))
     assert not np.any(np.isnan(np.delete(got, 50, axis=0)))
+
+
+# ------------------------------------------------------------------ prep ----
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_prep_bit_exact(wid):
+    w = workload(wid)
+    note(f"prep parity: workload {wid} ({w['name']}), {len(w['pos'])} rows")
+    qhat, st = gpu_prep(w)
+    assert st == 0
+    got = u16_host(qhat)
+    want = O.prep_queries(w["queries"], w["pos"], w["q_norm_w"], w["rotary_dim"], w["theta"],
+                          w["eps"])
+    diff = np.nonzero(got != want)
+    assert len(diff[0]) == 0, (len(diff[0]), got[diff][:8], want[diff][:8], diff[0][:8])
+
+
+def test_prep_nan_query_and_bad_positions():
+    w = workload(1)
+    pos = np.array([0, 5, 511, -1, 512, 77, 2**31 - 1], dtype=np.int32)
+    q = w["queries"][: len(pos)].copy()
+    q[1, 2, 9] = 0x7FC0   # NaN in one head: that head is NaN, the others finite
+    q[5, 0, 3] = 0xFFC1   # negative NaN with a payload: written as 0x7FC0
+    note("prep: NaN queries and out-of-range positions")
+    qhat, st = gpu_prep(w, pos=pos, q=q)
+    assert st == O.STATUS_BAD_POSITION
+    got = u16_host(qhat)
+    valid = [0, 1, 2, 5]
+    want = O.prep_queries(q[valid], pos[valid], w["q_norm_w"], w["rotary_dim"], w["theta"],
+                          w["eps"])
+    assert np.array_equal(got[valid], want)
+    assert np.all(got[1, 2] == 0x7FC0) and np.all(got[5, 0] == 0x7FC0)
+    assert not np.any(got[1, [0, 1, 3]] == 0x7FC0)
+    assert np.all(got[[3, 4, 6]] == 0)
+
+
+@pytest.mark.parametrize("rd", [0, 2, 36, 128])
+def test_prep_other_rotary_dims(rd):
+    w = workload(1)
+    rows = np.arange(0, 512, 7)
+    pos, q = w["pos"][rows], w["queries"][rows]
+    note(f"prep: rotary_dim {rd}")
+    ww = dict(w, rotary_dim=rd, theta=5e5)
+    qhat, st = gpu_prep(ww, pos=pos, q=q)
+    assert st == 0
+    want = O.prep_queries(q, pos, w["q_norm_w"], rd, 5e5, w["eps"])
+    assert np.array_equal(u16_host(qhat), want)
 
 
 # ---------------------------------------------------------------- select ----
@@ -157,19 +212,20 @@ def test_select_longest_supported_row():
 
 # ----------------------------------------------------------------- score ----
 
+@pytest.mark.parametrize("path", ["fused", "prepped"])
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
-def test_score_within_bound_and_prefix_only(wid):
+def test_score_within_bound_and_prefix_only(wid, path):
     w = workload(wid)
     rows = sample_rows(wid)
     T = w["tokens"]
     cols = T // 4 + (7 if wid in (1, 3) else 0)
-    note(f"score parity: workload {wid}, {len(rows)} rows, score_cols {cols}")
+    note(f"score parity ({path}): workload {wid}, {len(rows)} rows, score_cols {cols}")
     pooled = u16_dev(oracle_pooled(wid))
     sentinel = np.float32(-7.25)
-    got, st = gpu_scores(w, pooled, pos=w["pos"][rows], q=w["queries"][rows], score_cols=cols,
-                         sentinel=sentinel)
+    got, st = SCORERS[path](w, pooled, pos=w["pos"][rows], q=w["queries"][rows], score_cols=cols,
+                            sentinel=sentinel)
     assert st == 0
-    want = oracle_scores(wid, rows)
+    want = oracle_sample_scores(wid)
     worst = 0.0
     for r, s in enumerate(want):
         n = len(s)
@@ -181,6 +237,18 @@ def test_score_within_bound_and_prefix_only(wid):
     assert worst <= SCORE_ATOL
 
 
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_score_prepped_equals_fused_bitwise(wid):
+    w = workload(wid)
+    rows = sample_rows(wid)
+    note(f"score: prepped vs fused, workload {wid}")
+    pooled = u16_dev(oracle_pooled(wid))
+    a, s1 = gpu_scores(w, pooled, pos=w["pos"][rows], q=w["queries"][rows])
+    b, s2 = gpu_scores_prepped(w, pooled, pos=w["pos"][rows], q=w["queries"][rows])
+    assert s1 == s2 == 0
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_score_duplicate_blocks_tie_exactly():
     w = workload(1)
     pooled = u16_dev(oracle_pooled(1))
@@ -190,13 +258,15 @@ def test_score_duplicate_blocks_tie_exactly():
         assert np.array_equal(got[vis, b].view(np.uint32), got[vis, b - 1].view(np.uint32))
 
 
-def test_score_nan_key_and_bad_positions():
+@pytest.mark.parametrize("path", ["fused", "prepped"])
+def test_score_nan_key_and_bad_positions(path):
     w = workload(1)
     pooled = oracle_pooled(1).copy()
     pooled[50] = 0x7FC0
     pos = np.array([199, 200, 202, 203, 204, 511, -3, 512, 700], dtype=np.int32)
     q = w["queries"][: len(pos)]
-    got, st = gpu_scores(w, u16_dev(pooled), pos=pos, q=q)
+    note(f"score ({path}): NaN key, bad positions")
+    got, st = SCORERS[path](w, u16_dev(pooled), pos=pos, q=q)
     assert st == O.STATUS_BAD_POSITION
     for r, p in enumerate(pos):
         if not 0 <= p < 512:
@@ -221,12 +291,12 @@ def test_end_to_end_masks(wid):
     if len(w["dup_blocks"]):
         p = u16_host(pooled_dev)
         pooled_dev = u16_dev(synth.apply_dups(p, w["dup_blocks"]))
-    scores, st = gpu_scores(w, pooled_dev)
+    scores, st = gpu_scores_prepped(w, pooled_dev)
     assert st == 0
     mask, st = gpu_select(scores, cols, w["pos"], T, w["budget"])
     assert st == 0
     rows = sample_rows(wid)
-    want_scores = oracle_scores(wid, rows)
+    want_scores = oracle_sample_scores(wid)
     want_dense = dense(want_scores, cols)
     want_mask, _ = O.select_mask(want_dense, cols, w["pos"][rows], T, w["budget"])
     loose = 0
