@@ -56,13 +56,64 @@ __device__ __forceinline__ bool is_finite_bits(float s) {
   return (__float_as_uint(s) & 0x7F800000u) != 0x7F800000u;
 }
 
+// cos and sin, in double, of an angle given as a float with |angle| < 2^18.
+// Cody-Waite reduction (Cody and Waite, "Software Manual for the Elementary
+// Functions", 1980): k = nearest integer to angle * 2/pi, r = angle - k pi/2
+// with pi/2 split in three parts, the first two of 35 significant bits so
+// that k * part is exact for |k| < 2^18.  sin r and cos r are their Taylor
+// series to r^17 and r^18 (|r| <= pi/4 + a rounding: the first omitted term
+// is below 1e-19 relative).  The quadrant k mod 4 then swaps and negates.
+__device__ __forceinline__ void cos_sin_small_angle(float angle, double& c, double& s) {
+#pragma clang fp contract(off)
+  constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  constexpr double kPio2a = 0x1.921fb54440000p+0;   // 35 bits
+  constexpr double kPio2b = 0x1.68c234c4c0000p-39;  // 35 bits
+  constexpr double kPio2c = 0x1.98a2e03707345p-77;
+  const double x = static_cast<double>(angle);
+  const double k = rint(x * kTwoOverPi);
+  double r = __builtin_fma(-k, kPio2a, x);
+  r = __builtin_fma(-k, kPio2b, r);
+  r = __builtin_fma(-k, kPio2c, r);
+  const double r2 = r * r;
+  // 1/n! for n = 2 .. 18
+  double ps = 0x1.952c77030ad4ap-49;               // 1/17!
+  ps = __builtin_fma(ps, r2, -0x1.ae7f3e733b81fp-41);  // -1/15!
+  ps = __builtin_fma(ps, r2, 0x1.6124613a86d09p-33);   // 1/13!
+  ps = __builtin_fma(ps, r2, -0x1.ae64567f544e4p-26);  // -1/11!
+  ps = __builtin_fma(ps, r2, 0x1.71de3a556c734p-19);   // 1/9!
+  ps = __builtin_fma(ps, r2, -0x1.a01a01a01a01ap-13);  // -1/7!
+  ps = __builtin_fma(ps, r2, 0x1.1111111111111p-7);    // 1/5!
+  ps = __builtin_fma(ps, r2, -0x1.5555555555555p-3);   // -1/3!
+  const double sr = __builtin_fma(r * r2, ps, r);
+  double pc = 0x1.6827863b97d97p-53;               // 1/18!
+  pc = __builtin_fma(pc, r2, -0x1.ae7f3e733b81fp-45);  // -1/16!
+  pc = __builtin_fma(pc, r2, 0x1.93974a8c07c9dp-37);   // 1/14!
+  pc = __builtin_fma(pc, r2, -0x1.1eed8eff8d898p-29);  // -1/12!
+  pc = __builtin_fma(pc, r2, 0x1.27e4fb7789f5cp-22);   // 1/10!
+  pc = __builtin_fma(pc, r2, -0x1.a01a01a01a01ap-16);  // -1/8!
+  pc = __builtin_fma(pc, r2, 0x1.6c16c16c16c17p-10);   // 1/6!
+  pc = __builtin_fma(pc, r2, -0x1.5555555555555p-5);   // -1/4!
+  pc = __builtin_fma(pc, r2, 0x1.0000000000000p-1);    // 1/2!
+  const double cr = __builtin_fma(-r2, pc, 1.0);
+  const int q = static_cast<int>(static_cast<int64_t>(k)) & 3;
+  const double c0 = (q & 1) ? sr : cr;
+  const double s0 = (q & 1) ? cr : sr;
+  c = (q == 1 || q == 2) ? -c0 : c0;
+  s = (q & 2) ? -s0 : s0;
+}
+
 // Rotary angle of position `p` at frequency `f`: one f32 product, then cos
 // and sin evaluated in double on that f32 angle and rounded to f32 and bf16.
+// Positions below 2^18 with frequencies at most 1 keep |angle| < 2^18; any
+// other angle goes through the library cos/sin.
 __device__ __forceinline__ void rope_cos_sin(int64_t p, float f, float& c, float& s) {
 #pragma clang fp contract(off)
   const float angle = static_cast<float>(p) * f;
   double sd, cd;
-  sincos(static_cast<double>(angle), &sd, &cd);
+  if (fabsf(angle) < 262144.0f)
+    cos_sin_small_angle(angle, cd, sd);
+  else
+    sincos(static_cast<double>(angle), &sd, &cd);
   c = round_bf16(static_cast<float>(cd));
   s = round_bf16(static_cast<float>(sd));
 }
