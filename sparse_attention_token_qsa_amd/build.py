@@ -28,6 +28,8 @@ FLAGS = [
     "-fPIC",
     # keep the compiler from emitting packed f32 math
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the epilogue reads them directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]

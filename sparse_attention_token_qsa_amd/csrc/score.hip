@@ -12,12 +12,20 @@
 // relu / head-sum / scale epilogue never leaves the lane.  This is the shape
 // the pages' SIMT kernel avoided on 16x8 tiles; 32-row M tiles fit it exactly.
 //
-// Workgroup: 4 waves.  WM waves stack along M (8 query rows = 32 M-rows per
-// wave), WN = 4 / WM waves stack along N (64 blocks = two 32-block MFMA
-// tiles per wave).  Query prep runs once per workgroup into LDS; each wave
-// keeps its A fragments (8 x 16 B) in registers for the whole block loop.
-// Pooled-key tiles are staged in LDS with a 272-byte row pitch so the
-// 32 distinct rows one B-fragment read touches fall in distinct banks.
+// Workgroup: 4 waves.  WM waves stack along M, each holding MS M-subtiles
+// (8 query rows = 32 M-rows each) as A fragments in registers for the whole
+// block loop; WN = 4 / WM waves stack along N, one 32-block MFMA tile each
+// per step.  Every B fragment read from LDS feeds MS MFMAs.  The queries come
+// either prepared (qsa_prep_queries) straight from memory into the A
+// fragments, or are normed and roped in a per-workgroup LDS prologue.
+//
+// Key tiles stream through a ring of D LDS stages, loaded by the memory
+// engine straight into LDS (global_load_lds_dwordx4: no register staging)
+// D - 1 steps ahead of their MFMAs.  A stage holds TILE 256-byte block rows
+// with the 16-byte chunk c of row r stored at chunk c ^ (r & 7), so the 32
+// rows one B-fragment read touches spread over all banks.  Loads and the
+// branch-free score stores retire in issue order, so each step waits only
+// for its own tile's loads, not for the stores issued after them.
 // A workgroup walks a contiguous range of block tiles and stops at the
 // largest visible block count of its rows (causal prefill rows are ragged).
 #include "qsa_device.h"
@@ -30,7 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kScoreThreads = 256;
-constexpr int kPitch = 136;  // LDS row pitch in bf16 elements (272 bytes)
+constexpr int kPitch = 136;  // prologue LDS row pitch in bf16 elements (272 bytes)
 constexpr float kScale = static_cast<float>(0.088388347648318440550);  // 1/sqrt(128)
 
 struct ScoreArgs {
@@ -45,15 +53,23 @@ struct ScoreArgs {
   float* scores;
   int64_t score_cols;
   int32_t* status;
-  int64_t tiles_per_split;
+  int64_t splits;  // workgroups per row group; split s takes tiles s, s + splits, ...
   int64_t row_groups;
   int64_t tasks;
   int q_vec;
-  int pooled_vec;  // pooled keys 16-byte aligned (host-side choice of kernel)
   RopeParams rp;
 };
 
 __device__ __forceinline__ float relu_keep_nan(float x) { return x < 0.0f ? 0.0f : x; }
+
+// Waits on the vector-memory counter only (expcnt / lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Waits until this wave's LDS operations have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (3 << 14)); }
 
 // Sum over the 16 lanes of a DPP row, returned in all 16 (rotations 8, 4, 2,
 // 1).  Used on sums of squares of bf16 values, which are exact in double in
@@ -91,34 +107,36 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 u, float (&v)[8]) {
   }
 }
 
-// Workgroup geometry.  WM waves along M (8 query rows = 32 M-rows each),
-// WN = 4 / WM waves along N, NS 32-block MFMA tiles per wave and step.
-template <int WM, int NS>
+// Workgroup geometry.
+template <int WM, int MS, int D, bool PREP>
 struct ScoreGeom {
   static constexpr int WN = 4 / WM;
-  static constexpr int RG = 8 * WM;            // query rows per workgroup
-  static constexpr int TILE = 32 * NS * WN;    // blocks per step
-  static constexpr int NPASS = RG * 4 / 16;    // head vectors per 16-lane group
-  static constexpr int kChunks = TILE * 16 / kScoreThreads;  // 16-byte loads per thread per tile
+  static constexpr int RG = 8 * MS * WM;       // query rows per workgroup
+  static constexpr int TILE = 32 * WN;         // blocks per step
+  static constexpr int NPASS = RG * 4 / 16;    // head vectors per 16-lane group (prologue)
+  static constexpr int kLoads = TILE / 16;     // 1 KiB LDS loads per wave per tile
+  static constexpr int kStores = 4 * MS;       // score stores per wave per step
+  static constexpr int kStageBytes = TILE * 256;
   // prologue: normed + roped queries, then packed bf16 (cos, sin) per row and frequency
   static constexpr int kQBytes = RG * 4 * kPitch * 2;
-  static constexpr int kPrologueBytes = kQBytes + RG * kMaxHalfRotary * 4;
-  // block loop: two key tiles
-  static constexpr int kTileBytes = TILE * kPitch * 2;
-  static constexpr int kBytes = kPrologueBytes > 2 * kTileBytes ? kPrologueBytes : 2 * kTileBytes;
+  static constexpr int kPrologueBytes = PREP ? 0 : kQBytes + RG * kMaxHalfRotary * 4;
+  static constexpr int kRingBytes = D * kStageBytes;
+  static constexpr int kBytes = kPrologueBytes > kRingBytes ? kPrologueBytes : kRingBytes;
 };
 
-template <int WM, int NS, bool VECP, bool BUFST, bool PREP>
+template <int WM, int MS, int D, bool BUFST, bool PREP>
 __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreArgs a) {
-  using G = ScoreGeom<WM, NS>;
+  using G = ScoreGeom<WM, MS, D, PREP>;
   constexpr int RG = G::RG;
   constexpr int TILE = G::TILE;
   constexpr int NPASS = G::NPASS;
-  constexpr int KC = G::kChunks;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PREP ? 2 * G::kTileBytes : G::kBytes];
+  static_assert(RG <= 64, "wave 0 holds one row per lane");
+  static_assert(D >= 3, "the ring needs a stage in use, one landing and one ahead");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::kBytes];
   __shared__ int nvis[RG];
   __shared__ int ppos[RG];
   __shared__ int sh_nmax;
+  __shared__ int sh_nmin;
 
   uint16_t(*qs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem);
   uint32_t(*csq)[kMaxHalfRotary] = reinterpret_cast<uint32_t(*)[kMaxHalfRotary]>(smem + G::kQBytes);
@@ -127,73 +145,36 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // Task order: tasks that share a block range are kept on one XCD (the
-  // hardware deals consecutive workgroups round-robin over 8 XCDs), so each
-  // XCD's L2 holds only its share of the pooled keys.
+  // Task order: the splits of a row group take interleaved tiles, so at any
+  // moment they write neighbouring 256-byte pieces of the same score rows;
+  // consecutive tasks (the splits of one row group) are kept on one XCD (the
+  // hardware deals consecutive workgroups round-robin over 8 XCDs), so those
+  // pieces meet in one L2 and leave it as whole lines and pages.
   int64_t task = blockIdx.x;
   {
     const int64_t per = a.tasks >> 3;
     if (task < (per << 3)) task = (task & 7) * per + (task >> 3);
   }
-  const int64_t rg = task % a.row_groups;
-  const int64_t split = task / a.row_groups;
+  const int64_t rg = task / a.splits;
+  const int64_t split = task - rg * a.splits;
   const int64_t row0 = rg * RG;
-  const int nb_total = static_cast<int>(a.tokens / kRatio);
-  const int blk_begin = static_cast<int>(split * a.tiles_per_split * TILE);
-  const int blk_stop = static_cast<int>(min((split + 1) * a.tiles_per_split * TILE, static_cast<int64_t>(nb_total)));
+  const int blk_begin = static_cast<int>(split) * TILE;
+  const int stride = static_cast<int>(a.splits) * TILE;
 
-  // ---- key tiles: 16-byte chunks of a tile, held in registers from their
-  // load until they are written to LDS.  Block indices are clamped to the
-  // last block the workgroup may use, so loads never leave the cache and
-  // every step issues the same loads; blocks past the end are never stored.
-  auto fetch = [&](uint4 (&dst)[KC], int nb0, int last) {
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int idx = tid + i * kScoreThreads;
-      int bb = nb0 + (idx >> 4);
-      bb = bb < last ? bb : last;
-      const uint16_t* src = a.pooled + static_cast<int64_t>(bb) * kHeadDim + 8 * (idx & 15);
-      if constexpr (VECP) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        dst[i].x = v.x;
-        dst[i].y = v.y;
-        dst[i].z = v.z;
-        dst[i].w = v.w;
-      } else {
-        dst[i].x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
-        dst[i].y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
-        dst[i].z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
-        dst[i].w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
-      }
-    }
-  };
-  auto stash = [&](const uint4 (&src)[KC], int buf) {
-    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * G::kTileBytes);
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int idx = tid + i * kScoreThreads;
-      *reinterpret_cast<uint4*>(&bs[idx >> 4][8 * (idx & 15)]) = src[i];
-    }
-  };
-  uint4 pa[KC], pb[KC];
-  if (blk_begin < blk_stop) {
-    fetch(pa, blk_begin, blk_stop - 1);
-    fetch(pb, blk_begin + TILE, blk_stop - 1);
-  }
-
-  // ---- query loads: 16-lane group `hv_local` takes head vector
-  // pass * 16 + hv_local (= 4 * local_row + head), 8 channels per lane.
-  // Prepared queries are loaded straight into A fragments instead.
   const int m = wave % WM;
   const int ng = wave / WM;
   const int khalf = 8 * (lane >> 5);
-  bf16x8_t afrag[8];
+  bf16x8_t afrag[MS][8];
   if constexpr (PREP) {
-    int64_t rr = row0 + ((32 * m + (lane & 31)) >> 2);
-    rr = rr < a.rows ? rr : a.rows - 1;  // rows past the end are never stored
-    const uint16_t* src = a.qhat + rr * (kHeads * kHeadDim) + kHeadDim * (lane & 3) + khalf;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) afrag[ks] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ks);
+    for (int ms = 0; ms < MS; ++ms) {
+      int64_t rr = row0 + ((32 * (MS * m + ms) + (lane & 31)) >> 2);
+      rr = rr < a.rows ? rr : a.rows - 1;  // rows past the end are never stored
+      const uint16_t* src = a.qhat + rr * (kHeads * kHeadDim) + kHeadDim * (lane & 3) + khalf;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        afrag[ms][ks] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ks);
+    }
   }
   const int hv_local = tid >> 4;
   const int g = tid & 15;
@@ -221,7 +202,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
 
   // ---- positions and visible block counts (wave 0)
   if (wave == 0) {
-    int n = 0, p = 0;
+    int n = 0, p = 0, nlo = 0x7FFFFFFF;
     if (lane < RG) {
       const int64_t r = row0 + lane;
       if (r < a.rows) {
@@ -233,14 +214,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
       }
       nvis[lane] = n;
       ppos[lane] = p;
+      nlo = n;
     }
     const uint32_t mx = wave_max_u32(static_cast<uint32_t>(n));
-    if (lane == 0) sh_nmax = static_cast<int>(mx);
+    const uint32_t mn = wave_min_u32(static_cast<uint32_t>(nlo));
+    if (lane == 0) {
+      sh_nmax = static_cast<int>(mx);
+      sh_nmin = static_cast<int>(mn);
+    }
   }
   __syncthreads();
   const int nmax = sh_nmax;
-  if (blk_begin >= nmax) return;  // uniform across the workgroup
-  const int blk_end = blk_stop < nmax ? blk_stop : nmax;
+  const int nmin = sh_nmin;  // blocks every row of the workgroup sees
+  if (blk_begin >= nmax) return;  // uniform across the workgroup; nothing in flight to LDS
+  const int blk_end = nmax;
 
   if constexpr (!PREP) {
   // ---- cos/sin of every (row, frequency), four per thread in flight
@@ -333,87 +320,123 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   for (int p = 0; p < NPASS; ++p) *reinterpret_cast<uint4*>(&qs[p * 16 + hv_local][8 * g]) = outq[p];
   __syncthreads();
 
-  // ---- A fragments: this wave's 32 M-rows (8 query rows x 4 heads), K = 128.
+  // ---- A fragments: this wave's MS x 32 M-rows (8 query rows x 4 heads each), K = 128.
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    afrag[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[32 * m + (lane & 31)][16 * ks + khalf]);
-
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      afrag[ms][ks] = *reinterpret_cast<const bf16x8_t*>(
+          &qs[32 * (MS * m + ms) + (lane & 31)][16 * ks + khalf]);
+  __syncthreads();  // every wave holds its A fragments: the LDS becomes the key ring
   }
 
-  // per-lane output rows: this lane holds rows 8m + 2 q4 + (lane >> 5).
+  // ---- key ring.  Wave w loads rows [4 (w kL + i), +4) of a tile, i < kL:
+  // lane L of load i fills LDS bytes 1024 (w kL + i) + 16 L, i.e. row
+  // 4 (w kL + i) + L / 16 at chunk L % 16, which holds the key's chunk
+  // (L % 16) ^ (row & 7).  Block indices are clamped to the last block the
+  // workgroup may use, so loads never leave the cache and every step issues
+  // the same number of loads.
+  constexpr int kL = G::kLoads;
+  const int lrow = lane >> 4;
+  const int lchunk = lane & 15;
+  auto load_tile = [&](int nb0, int stage) {
+#pragma unroll
+    for (int i = 0; i < kL; ++i) {
+      const int row = 4 * (wave * kL + i) + lrow;
+      const int blk = min(nb0 + row, blk_end - 1);
+      const uint16_t* src = a.pooled + static_cast<int64_t>(blk) * kHeadDim + 8 * (lchunk ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       static_cast<void*>(smem + stage * G::kStageBytes + 1024 * (wave * kL + i)),
+                                       16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t);
+
+  // per-lane output rows: subtile ms holds rows 8 (MS m + ms) + 2 q4 + (lane >> 5).
   // With BUFST the stores go through a buffer resource over the workgroup's
-  // rows: a lane whose block is past its row's prefix gets an offset past
-  // the resource's end, and the hardware drops that store.  The stores then
-  // carry no branch, so the loads issued after them never wait behind them.
-  float* orow[4];
-  int ovis[4];
-  int ooff[4];
+  // rows, the lane's row and column in the vector offset and the step's first
+  // block in the scalar offset.  In a step that reaches past some row's
+  // prefix, a lane whose block is past its row's prefix gets an offset beyond
+  // the resource's end and the hardware drops that store.
+  const int col = ng * 32 + (lane & 31);
+  float* orow[MS][4];
+  int ovis[MS][4];
+  int ooff[MS][4];
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int lr = 8 * m + 2 * q4 + (lane >> 5);
-    orow[q4] = a.scores + (row0 + lr) * a.score_cols;
-    ovis[q4] = nvis[lr];
-    ooff[q4] = lr * static_cast<int>(a.score_cols) * 4;
-  }
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int lr = 8 * (MS * m + ms) + 2 * q4 + (lane >> 5);
+      orow[ms][q4] = a.scores + (row0 + lr) * a.score_cols;
+      ovis[ms][q4] = nvis[lr];
+      ooff[ms][q4] = (lr * static_cast<int>(a.score_cols) + col) * 4;
+    }
   __amdgpu_buffer_rsrc_t out_rsrc;
   if constexpr (BUFST)
     out_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.scores + row0 * a.score_cols, static_cast<short>(0),
                                                  static_cast<int>(RG * a.score_cols * 4), 0x00020000);
-  if constexpr (!PREP) __syncthreads();  // every wave holds its A fragments: the LDS becomes key tiles
-  stash(pa, 0);
-  __syncthreads();
+  // B-fragment address of this lane in a stage: row `col`, chunk 2 ks + (lane >> 5), swizzled.
+  const int brow = col * 256;
+  const int bsw = col & 7;
 
-  // ---- block loop.  Step t: LDS buffer t&1 holds tile t, one register set
-  // holds tile t+1; tile t+2 is loaded into the other set, the MFMAs run on
-  // tile t, tile t+1 goes to LDS, then tile t's scores are stored.  Loads are
-  // issued before the stores they must not wait behind.
-  const int col0 = ng * (32 * NS) + (lane & 31);
-  auto step = [&](int nb0, int buf, uint4 (&ld)[KC], uint4 (&st)[KC]) {
-    fetch(ld, nb0 + 2 * TILE, blk_end - 1);
-    uint16_t(*bs)[kPitch] = reinterpret_cast<uint16_t(*)[kPitch]>(smem + buf * G::kTileBytes);
-    f32x16_t acc[NS];
+  // tile 0 landed (the D - 2 later tiles may still be in flight)
+  wait_vmcnt<(D - 2) * kL>();
+  __builtin_amdgcn_s_barrier();
+
+  // ---- block loop: step t loads tile t + D - 1, runs tile t's MFMAs and
+  // stores its scores, then waits for tile t + 1.  Counting what this wave
+  // issued after tile t + 1's loads gives at least (D - 2) loads and one
+  // step's stores in every step, so vmcnt((D - 2) kL + kStores) retires them.
+  int stage = 0;
+  for (int nb0 = blk_begin; nb0 < blk_end; nb0 += stride) {
+    int lstage = stage + D - 1;
+    lstage = lstage >= D ? lstage - D : lstage;
+    load_tile(nb0 + (D - 1) * stride, lstage);
+    const unsigned char* sb = smem + stage * G::kStageBytes + brow;
+    f32x16_t acc[MS];
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[n][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) acc[ms][v] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t b =
+          *reinterpret_cast<const bf16x8_t*>(sb + 16 * ((2 * ks + (lane >> 5)) ^ bsw));
 #pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&bs[col0 + 32 * n][16 * ks + khalf]);
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], b, acc[n], 0, 0, 0);
-      }
+      for (int ms = 0; ms < MS; ++ms)
+        acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms][ks], b, acc[ms], 0, 0, 0);
     }
-    stash(st, buf ^ 1);
-    const int blk0 = nb0 + col0;
+    const bool whole = nb0 + TILE <= nmin;  // every lane's block is inside its row's prefix
+    const int blk = nb0 + col;
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      const int blk = blk0 + 32 * n;
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        float s = relu_keep_nan(acc[n][4 * q4 + 0]) + relu_keep_nan(acc[n][4 * q4 + 1]);
-        s = s + relu_keep_nan(acc[n][4 * q4 + 2]);
-        s = s + relu_keep_nan(acc[n][4 * q4 + 3]);
+        float s = relu_keep_nan(acc[ms][4 * q4 + 0]) + relu_keep_nan(acc[ms][4 * q4 + 1]);
+        s = s + relu_keep_nan(acc[ms][4 * q4 + 2]);
+        s = s + relu_keep_nan(acc[ms][4 * q4 + 3]);
         if constexpr (BUFST) {
-          const int off = blk < ovis[q4] ? ooff[q4] + 4 * blk : static_cast<int>(0x80000000u);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * kScale), out_rsrc, off, 0, 0);
+          const int off = (whole || blk < ovis[ms][q4]) ? ooff[ms][q4] : static_cast<int>(0x80000000u);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * kScale), out_rsrc, off, 4 * nb0, 0);
         } else {
-          if (blk < ovis[q4]) orow[q4][blk] = s * kScale;
+          if (blk < ovis[ms][q4]) orow[ms][q4][blk] = s * kScale;
         }
       }
-    }
-    __syncthreads();
-  };
-  for (int nb0 = blk_begin; nb0 < blk_end; nb0 += 2 * TILE) {
-    step(nb0, 0, pa, pb);
-    if (nb0 + TILE >= blk_end) break;
-    step(nb0 + TILE, 1, pb, pa);
+    wait_lgkm0();
+    if constexpr (BUFST)
+      wait_vmcnt<(D - 2) * kL + G::kStores>();
+    else
+      wait_vmcnt<0>();  // branchy stores: their count per step is not fixed
+    __builtin_amdgcn_s_barrier();
+    stage = stage + 1 == D ? 0 : stage + 1;
   }
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
-template <int WM, int NS, bool PREP>
+template <int WM, int MS, int D, bool PREP>
 hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
-  using G = ScoreGeom<WM, NS>;
+  using G = ScoreGeom<WM, MS, D, PREP>;
   ScoreArgs a = base;
   const int64_t nb_total = a.tokens / kRatio;
   a.row_groups = (a.rows + G::RG - 1) / G::RG;
@@ -424,30 +447,29 @@ hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
   int64_t splits = (1024 + a.row_groups - 1) / a.row_groups;
   if (splits < 1) splits = 1;
   if (splits > n_tiles) splits = n_tiles;
-  a.tiles_per_split = (n_tiles + splits - 1) / splits;
-  splits = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  a.splits = splits;
   a.tasks = a.row_groups * splits;
   if (a.tasks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(a.tasks));
   const dim3 block(kScoreThreads);
   // buffer-resource stores need the workgroup's rows within 2^31 bytes
-  const bool bufst = a.score_cols <= 0x7FFFFFFF / (4 * G::RG);
-  if (a.pooled_vec && bufst)
-    score_mfma_kernel<WM, NS, true, true, PREP><<<grid, block, 0, stream>>>(a);
-  else if (a.pooled_vec)
-    score_mfma_kernel<WM, NS, true, false, PREP><<<grid, block, 0, stream>>>(a);
-  else if (bufst)
-    score_mfma_kernel<WM, NS, false, true, PREP><<<grid, block, 0, stream>>>(a);
+  if (a.score_cols <= 0x7FFFFFFF / (4 * G::RG))
+    score_mfma_kernel<WM, MS, D, true, PREP><<<grid, block, 0, stream>>>(a);
   else
-    score_mfma_kernel<WM, NS, false, false, PREP><<<grid, block, 0, stream>>>(a);
+    score_mfma_kernel<WM, MS, D, false, PREP><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <bool PREP>
 hipError_t launch_score_rows(const ScoreArgs& a, hipStream_t stream) {
-  if (a.rows >= 32) return launch_score_geom<4, 2, PREP>(a, stream);
-  if (a.rows > 8) return launch_score_geom<2, 2, PREP>(a, stream);
-  return launch_score_geom<1, 1, PREP>(a, stream);
+  // Prepared queries: 32 rows per wave when there are enough rows, so each
+  // B fragment feeds four MFMAs.  The one-call path keeps 8 rows per wave,
+  // which bounds its query-prep LDS.
+  if constexpr (PREP)
+    if (a.rows >= 64) return launch_score_geom<2, 4, 4, PREP>(a, stream);
+  if (a.rows >= 32) return launch_score_geom<4, 1, 4, PREP>(a, stream);
+  if (a.rows > 8) return launch_score_geom<2, 1, 4, PREP>(a, stream);
+  return launch_score_geom<1, 1, 3, PREP>(a, stream);
 }
 
 }  // namespace
@@ -468,7 +490,6 @@ hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos,
   a.score_cols = score_cols;
   a.status = status;
   a.q_vec = (q_stride % 8 == 0) && (reinterpret_cast<uintptr_t>(q) % 16 == 0);
-  a.pooled_vec = reinterpret_cast<uintptr_t>(pooled) % 16 == 0;
   a.rp = rp;
   return launch_score_rows<false>(a, stream);
 }
@@ -485,7 +506,6 @@ hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_
   a.scores = scores;
   a.score_cols = score_cols;
   a.status = status;
-  a.pooled_vec = reinterpret_cast<uintptr_t>(pooled) % 16 == 0;
   return launch_score_rows<true>(a, stream);
 }
 
