@@ -40,6 +40,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kScoreThreads = 256;
 constexpr int kPitch = 136;  // prologue LDS row pitch in bf16 elements (272 bytes)
 constexpr float kScale = static_cast<float>(0.088388347648318440550);  // 1/sqrt(128)
+constexpr int kStoreNT = 2;  // buffer-store cache policy: nt
 
 struct ScoreArgs {
   const uint16_t* qhat;  // prepared queries [rows, 4, 128] bf16 (PREP kernels)
@@ -59,8 +60,6 @@ struct ScoreArgs {
   int q_vec;
   RopeParams rp;
 };
-
-__device__ __forceinline__ float relu_keep_nan(float x) { return x < 0.0f ? 0.0f : x; }
 
 // Waits on the vector-memory counter only (expcnt / lgkmcnt left at their maxima).
 template <int N>
@@ -407,22 +406,50 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
       for (int ms = 0; ms < MS; ++ms)
         acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms][ks], b, acc[ms], 0, 0, 0);
     }
-    const bool whole = nb0 + TILE <= nmin;  // every lane's block is inside its row's prefix
-    const int blk = nb0 + col;
+    // relu(d) = (d + |d|) / 2 exactly (0 or d; NaN stays NaN), so the head
+    // sum of the doubled terms is exactly twice the sum of the relu terms and
+    // one multiply by scale / 2 gives the same f32 score.  A -0.0 head term
+    // becomes +0.0, which only changes the sign of an all-zero score.
+    float sc[MS][4];
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        float s = relu_keep_nan(acc[ms][4 * q4 + 0]) + relu_keep_nan(acc[ms][4 * q4 + 1]);
-        s = s + relu_keep_nan(acc[ms][4 * q4 + 2]);
-        s = s + relu_keep_nan(acc[ms][4 * q4 + 3]);
-        if constexpr (BUFST) {
-          const int off = (whole || blk < ovis[ms][q4]) ? ooff[ms][q4] : static_cast<int>(0x80000000u);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * kScale), out_rsrc, off, 4 * nb0, 0);
-        } else {
-          if (blk < ovis[ms][q4]) orow[ms][q4][blk] = s * kScale;
-        }
+        const float h0 = acc[ms][4 * q4 + 0], h1 = acc[ms][4 * q4 + 1];
+        const float h2 = acc[ms][4 * q4 + 2], h3 = acc[ms][4 * q4 + 3];
+        float s = (h0 + fabsf(h0)) + (h1 + fabsf(h1));
+        s = s + (h2 + fabsf(h2));
+        s = s + (h3 + fabsf(h3));
+        sc[ms][q4] = s * (0.5f * kScale);
       }
+    const int blk = nb0 + col;
+    if (nb0 + TILE <= nmin) {  // every lane's block is inside its row's prefix
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if constexpr (BUFST) {
+            // non-temporal: the score stream is written once and read back once
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[ms][q4]), out_rsrc, ooff[ms][q4],
+                                                  4 * nb0, kStoreNT);
+          } else {
+            orow[ms][q4][blk] = sc[ms][q4];
+          }
+        }
+    } else {
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if constexpr (BUFST) {
+            const int off = blk < ovis[ms][q4] ? ooff[ms][q4] : static_cast<int>(0x80000000u);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[ms][q4]), out_rsrc, off, 4 * nb0,
+                                                  kStoreNT);
+          } else {
+            if (blk < ovis[ms][q4]) orow[ms][q4][blk] = sc[ms][q4];
+          }
+        }
+    }
     wait_lgkm0();
     if constexpr (BUFST)
       wait_vmcnt<(D - 2) * kL + G::kStores>();
