@@ -15,17 +15,19 @@
 // composite: selection is one threshold, ties included.
 //
 // One workgroup per row; the row's keys live in registers (KPT per thread).
-//  1. Long rows (1024 threads): every thread's largest key is a distinct
-//     key; taking in each wave the r-th largest of the 64 thread maxima,
-//     r = ceil(keep / waves), and the minimum L of those over the waves, at
-//     least keep keys are >= L.  So C* >= L << 32 and only keys >= L can be
-//     kept.  They are compacted into LDS (typically ~1k of 16k-64k).
+//  1. Long rows: every thread takes the TOPM-th largest of its own keys; in
+//     each wave the r-th largest of those 64 values, r = ceil(keep / (waves
+//     * TOPM)), is found by a bitwise search over ballots, and the minimum L
+//     over the waves leaves at least keep keys >= L.  So C* >= L << 32 and
+//     only keys >= L can be kept.  They are compacted into LDS (typically
+//     ~1k of 16k-64k).
 //  2. Radix select of C* over the candidates (the compacted list, or all
 //     keys when the list would overflow or the row is short), 8 bits per
-//     pass starting just below the common prefix of the candidates' smallest
-//     and largest composite, so the first histogram is not crowded into the
-//     few exponent bins the scores occupy.  A pass ends the search early once
-//     every candidate of the chosen bin is taken; the returned bin floor then
+//     pass starting just below the bits every candidate shares.  A pass is
+//     one barrier: the histograms rotate through three LDS buffers (fill
+//     one, clear the next), and every wave scans the filled one with DPP and
+//     picks the digit itself.  A pass ends the search early once every
+//     candidate of the chosen bin is taken; the returned bin floor then
 //     separates the candidates, and `lowkey` excludes the non-candidates.
 //  3. Each thread writes its blocks' mask bytes (16 bytes per 4 blocks), the
 //     tail and the zero run from the same loop.
@@ -45,8 +47,6 @@ struct SelectArgs {
   int32_t* status;
 };
 
-constexpr int kCandCap = 4096;
-
 // A register copy the compiler cannot see through: values derived from it
 // are computed where they are used instead of being hoisted and kept live
 // (64 keys per thread leave no room for 64 precomputed 64-bit composites).
@@ -58,6 +58,18 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 __device__ __forceinline__ uint64_t composite(uint32_t key, int b) {
   return (static_cast<uint64_t>(key) << 32) |
          static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(b));
+}
+
+// The r-th largest (1 <= r <= 64) of the wave's 64 values, in every lane:
+// the largest x with at least r lanes holding a value >= x, built bit by bit.
+__device__ __forceinline__ uint32_t wave_rth_largest(uint32_t v, int r) {
+  uint32_t x = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = x | (1u << bit);
+    if (__popcll(__ballot(v >= c)) >= r) x = c;
+  }
+  return x;
 }
 
 // Mask word of the token group [4w, 4w+4) outside the selected blocks: 1 for
@@ -88,94 +100,61 @@ __device__ __forceinline__ void write_prefix_row(uint8_t* mrow, int64_t tokens, 
   }
 }
 
-// Radix search for the keep-th largest composite among a candidate set.
-// `each(f)` calls f(composite) for every candidate this thread owns.
-// Returns C* (or the floor of a bin whose candidates are all taken: the same
-// kept set among the candidates).  All threads return the same value.
+// Radix search for the keep-th largest composite among a candidate set whose
+// composites all lie in [lo, hi].  `each(f)` calls f(composite) for every
+// candidate this thread owns.  hist holds three 256-bin buffers; the first
+// must be zero on entry (with a barrier since).  Returns C* (or the floor of
+// a bin whose candidates are all taken: the same kept set among the
+// candidates); every thread returns the same value.
 template <int NT, typename Each>
-__device__ uint64_t radix_threshold(Each each, uint32_t k, uint32_t* hist, uint64_t* red64) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ uint32_t sh_digit, sh_above, sh_count;
-  // smallest and largest candidate composite
-  uint64_t lo = ~0ull, hi = 0ull;
-  each([&](uint64_t c) {
-    lo = c < lo ? c : lo;
-    hi = c > hi ? c : hi;
-  });
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t l2 = __shfl_xor(lo, off), h2 = __shfl_xor(hi, off);
-    lo = l2 < lo ? l2 : lo;
-    hi = h2 > hi ? h2 : hi;
-  }
-  __syncthreads();
-  if (lane == 0) {
-    red64[wave] = lo;
-    red64[NW + wave] = hi;
-  }
-  __syncthreads();
-  lo = red64[0];
-  hi = red64[NW];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    lo = red64[w] < lo ? red64[w] : lo;
-    hi = red64[NW + w] > hi ? red64[NW + w] : hi;
-  }
-  if (lo == hi) return hi;  // a single candidate
-  int top = 63 - __clzll(lo ^ hi);  // highest bit that differs among candidates
+__device__ uint64_t radix_threshold(Each each, uint32_t k, uint64_t lo, uint64_t hi, uint32_t* hist) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (lo == hi) return hi;
+  int top = 63 - __clzll(lo ^ hi);                 // highest bit not shared by every candidate
   uint64_t prefix = hi & ~((2ull << top) - 1ull);  // the shared bits above `top`
-  while (true) {
+  for (int pass = 0;; ++pass) {
+    uint32_t* h = hist + 256 * (pass % 3);
+    uint32_t* next = hist + 256 * ((pass + 1) % 3);
     const int shift = top >= 7 ? top - 7 : 0;
     const int width = top - shift + 1;
     const uint64_t himask = ~((2ull << top) - 1ull);  // bits above the digit
-    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-    __syncthreads();
     each([&](uint64_t c) {
-      if ((c & himask) == prefix) atomicAdd(&hist[(c >> shift) & ((1u << width) - 1u)], 1u);
+      if ((c & himask) == prefix) atomicAdd(&h[(c >> shift) & ((1u << width) - 1u)], 1u);
     });
+    for (int i = tid; i < 256; i += NT) next[i] = 0u;
     __syncthreads();
-    if (wave == 0) {
-      uint32_t h[4], tot = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[i] = hist[4 * lane + i];
-        tot += h[i];
-      }
-      uint32_t incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(incl, off);
-        if (lane + off < 64) incl += v;
-      }
-      uint32_t above = incl - tot;
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (above < k && above + h[i] >= k) {
-          sh_digit = 4 * lane + i;
-          sh_above = above;
-          sh_count = h[i];
-        }
-        above += h[i];
-      }
-    }
-    __syncthreads();
-    const uint32_t d = sh_digit, above = sh_above, count = sh_count;
-    __syncthreads();  // hist and the sh_ words are rewritten by the next pass
-    prefix |= static_cast<uint64_t>(d) << shift;
+    // every wave: lane l holds bins 4l..4l+3; "above" counts larger digits
+    const uint4 hv = reinterpret_cast<const uint4*>(h)[lane];
+    const uint32_t tot = hv.x + hv.y + hv.z + hv.w;
+    const uint32_t incl = wave_incl_sum(tot);
+    const uint32_t total = read_lane(incl, 63);
+    const uint32_t a3 = total - incl;
+    const uint32_t a2 = a3 + hv.w, a1 = a2 + hv.z, a0 = a1 + hv.y;
+    uint32_t digit = 0, above = 0, count = 0;
+    bool found = false;
+    if (a3 < k && k <= a3 + hv.w) { digit = 4 * lane + 3; above = a3; count = hv.w; found = true; }
+    if (a2 < k && k <= a2 + hv.z) { digit = 4 * lane + 2; above = a2; count = hv.z; found = true; }
+    if (a1 < k && k <= a1 + hv.y) { digit = 4 * lane + 1; above = a1; count = hv.y; found = true; }
+    if (a0 < k && k <= a0 + hv.x) { digit = 4 * lane + 0; above = a0; count = hv.x; found = true; }
+    const int src = __ffsll(static_cast<unsigned long long>(__ballot(found))) - 1;
+    digit = read_lane(digit, src);
+    above = read_lane(above, src);
+    count = read_lane(count, src);
+    prefix |= static_cast<uint64_t>(digit) << shift;
     k -= above;
-    if (count == k || shift == 0) return prefix;  // every candidate of bin d is taken
+    if (count == k || shift == 0) return prefix;  // every candidate of bin `digit` is taken
     top = shift - 1;
   }
 }
 
-template <int NT, int KPT, bool VEC>
+template <int NT, int KPT, int TOPM, bool VEC>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   constexpr int NW = NT / 64;
-  constexpr bool kPrefilter = (NT == 1024);
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t red[NW];
-  __shared__ uint64_t red64[2 * NW];
+  // The prefilter's per-wave rank r = ceil(512 / (NW * TOPM)) must stay <= 32.
+  constexpr bool kPrefilter = NW * TOPM >= 16;
+  constexpr int kCandCap = NT >= 1024 ? 4096 : 2048;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[3 * 256];
+  __shared__ uint32_t red[2 * NW];
   __shared__ uint64_t cand[kPrefilter ? kCandCap : 1];
 
   const int tid = threadIdx.x;
@@ -241,6 +220,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = 0u;
   }
+  if (tid < 256) hist[tid] = 0u;  // first radix buffer; the next barrier publishes it
   if (__syncthreads_or(bad)) {
     write_prefix_row<NT, VEC>(mrow, T, -1);
     if (tid == 0) atomicOr(a.status, 2);
@@ -258,42 +238,33 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   uint32_t lowkey = 1u;
   bool done = false;
   if constexpr (kPrefilter) {
-    if (n >= 4 * NT) {  // every thread owns at least one visible block
-      uint32_t tmax = 0;
+    if (n >= 4 * NT) {  // every thread owns at least four visible blocks
+      uint32_t t1 = 0u, t2 = 0u;  // this thread's largest and TOPM-th largest key
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) tmax = key[j] > tmax ? key[j] : tmax;
-      // r-th largest thread maximum of this wave: bitonic sort, descending
-      const int r = (keep + NW - 1) / NW;
-      uint32_t v = tmax;
-#pragma unroll
-      for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride >= 1; stride >>= 1) {
-          const uint32_t o = __shfl_xor(v, stride);
-          const bool desc = ((lane & size) == 0) || size == 64;
-          const bool lower = ((lane & stride) == 0);
-          const bool take_max = (desc == lower);
-          v = take_max ? (o > v ? o : v) : (o < v ? o : v);
-        }
+      for (int j = 0; j < KPT; ++j) {
+        if constexpr (TOPM == 2) t2 = max(t2, min(t1, key[j]));
+        t1 = max(t1, key[j]);
       }
-      const uint32_t lw = __shfl(v, r - 1);
+      const int r = (keep + NW * TOPM - 1) / (NW * TOPM);
+      const uint32_t lw = wave_rth_largest(TOPM == 2 ? t2 : t1, r);
+      const uint32_t wmax = wave_max_u32(t1);
+      if (lane == 0) {
+        red[wave] = lw;
+        red[NW + wave] = wmax;
+      }
       __syncthreads();
-      if (lane == 0) red[wave] = lw;
-      __syncthreads();
-      uint32_t L = red[0];
+      uint32_t L = red[0], kmax = red[NW];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) L = red[w] < L ? red[w] : L;
+      for (int w = 1; w < NW; ++w) {
+        L = red[w] < L ? red[w] : L;
+        kmax = red[NW + w] > kmax ? red[NW + w] : kmax;
+      }
       // count and compact the candidates key >= L
       uint32_t mine = 0;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) mine += key[j] >= L ? 1u : 0u;
-      uint32_t incl = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      __syncthreads();
+      const uint32_t incl = wave_incl_sum(mine);
+      __syncthreads();  // every wave has read red[]
       if (lane == 63) red[wave] = incl;
       __syncthreads();
       uint32_t base = 0, total = 0;
@@ -317,13 +288,36 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
             [&](auto f) {
               for (int i = tid; i < c; i += NT) f(cand[i]);
             },
-            static_cast<uint32_t>(keep), hist, red64);
+            static_cast<uint32_t>(keep), static_cast<uint64_t>(L) << 32,
+            (static_cast<uint64_t>(kmax) << 32) | 0xFFFFFFFFull, hist);
         lowkey = L;
         done = true;
       }
     }
   }
   if (!done) {
+    // exact smallest and largest present key bound the composites
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      kmin = key[j] != 0u && key[j] < kmin ? key[j] : kmin;
+      kmax = key[j] > kmax ? key[j] : kmax;
+    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    __syncthreads();  // red[] may still be read by the prefilter
+    if (lane == 0) {
+      red[wave] = kmin;
+      red[NW + wave] = kmax;
+    }
+    __syncthreads();
+    kmin = red[0];
+    kmax = red[NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      kmin = red[w] < kmin ? red[w] : kmin;
+      kmax = red[NW + w] > kmax ? red[NW + w] : kmax;
+    }
     cstar = radix_threshold<NT>(
         [&](auto f) {
           // An opaque copy of the thread index: the composites are rebuilt in
@@ -337,7 +331,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
             if (kk != 0u) f(composite(kk, b));
           }
         },
-        static_cast<uint32_t>(keep), hist, red64);
+        static_cast<uint32_t>(keep), static_cast<uint64_t>(kmin) << 32,
+        (static_cast<uint64_t>(kmax) << 32) | 0xFFFFFFFFull, hist);
   }
 
   // ---- mask: kept blocks, the tail [4n, p] and zeros; every 16-byte chunk
@@ -379,12 +374,12 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   }
 }
 
-template <int NT, int KPT>
+template <int NT, int KPT, int TOPM>
 hipError_t launch_select_t(const SelectArgs& a, int64_t rows, bool vec, hipStream_t stream) {
   if (vec)
-    select_kernel<NT, KPT, true><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+    select_kernel<NT, KPT, TOPM, true><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
   else
-    select_kernel<NT, KPT, false><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+    select_kernel<NT, KPT, TOPM, false><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -406,13 +401,13 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
                    (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
   const int64_t nmax = tokens / kRatio;
   if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (nmax <= 1024) return launch_select_t<256, 4>(a, rows, vec, stream);
-  if (nmax <= 2048) return launch_select_t<256, 8>(a, rows, vec, stream);
-  if (nmax <= 4096) return launch_select_t<256, 16>(a, rows, vec, stream);
-  if (nmax <= 8192) return launch_select_t<1024, 8>(a, rows, vec, stream);
-  if (nmax <= 16384) return launch_select_t<1024, 16>(a, rows, vec, stream);
-  if (nmax <= 32768) return launch_select_t<1024, 32>(a, rows, vec, stream);
-  if (nmax <= 65536) return launch_select_t<1024, 64>(a, rows, vec, stream);
+  if (nmax <= 1024) return launch_select_t<256, 4, 1>(a, rows, vec, stream);
+  if (nmax <= 2048) return launch_select_t<256, 8, 1>(a, rows, vec, stream);
+  if (nmax <= 4096) return launch_select_t<256, 16, 1>(a, rows, vec, stream);
+  if (nmax <= 8192) return launch_select_t<512, 16, 2>(a, rows, vec, stream);
+  if (nmax <= 16384) return launch_select_t<512, 32, 2>(a, rows, vec, stream);
+  if (nmax <= 32768) return launch_select_t<1024, 32, 1>(a, rows, vec, stream);
+  if (nmax <= 65536) return launch_select_t<1024, 64, 1>(a, rows, vec, stream);
   return hipErrorInvalidValue;
 }
 
