@@ -126,6 +126,69 @@ def time_steps(d: Device, steps: int, warmup: int, torch):
     return wall, per
 
 
+def prime(torch):
+    """Keep the GPU busy for ~2 ms so the host can queue a whole measured
+    sequence ahead of it: small launches then run back to back on the GPU
+    instead of waiting for the Python binding's per-call host time."""
+    torch.cuda._sleep(4_000_000)
+
+
+def back_to_back_us(d: Device, torch, reps: int = 20):
+    """Per-launch microseconds of each stage launched `reps` times back to back
+    between one pair of HIP events, queued behind a busy GPU (no event between
+    launches: an event pair costs ~4.5 us of GPU time around a single launch)."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn in (("pool", d.pool), ("prep", d.prep), ("score", d.score), ("select", d.select)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        prime(torch)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(a.elapsed_time(b) * 1e3 / reps, 3)
+    return out
+
+
+def cold_step_us(d: Device, torch, reps: int = 10):
+    """Whole-step microseconds (pool, prep, score, select back to back) with L2
+    and MALL flushed before every step by a 512 MiB write, which also keeps the
+    GPU busy while the host queues the step; one HIP event pair around each
+    step, so the figure includes the launch gaps and one event pair's GPU
+    overhead and is an upper bound on the kernels' cold time."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ts = []
+    for i in range(reps + 2):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        d.pool()
+        d.prep()
+        d.score()
+        d.select()
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(a.elapsed_time(b) * 1e3)
+    # the same bracket around nothing: the event pair's own GPU time
+    fl = []
+    for i in range(reps + 2):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            fl.append(a.elapsed_time(b) * 1e3)
+    del flush
+    return round(sum(ts) / len(ts), 2), round(sum(fl) / len(fl), 2)
+
+
 def median(xs):
     s = sorted(xs)
     n = len(s)
@@ -224,7 +287,9 @@ def cpu_baseline(w, budget_s: float):
 
 def side_figures(torch, qsa, synth):
     """select+mask us/row on the 64k/256k decode workloads and the one-row
-    64k/256k shapes; per-kernel event means over 20 launches after 5 warm-ups."""
+    64k/256k shapes: per-kernel event means over 20 launches after 5 warm-ups
+    (each launch between its own event pair), per-kernel back-to-back launch
+    times, and the cold-cache step with its aggregate HBM fraction."""
     out = {}
     for key, w in (("decode_64k_x64", synth.make_workload(3)),
                    ("decode_256k_x16", synth.make_workload(4)),
@@ -233,10 +298,20 @@ def side_figures(torch, qsa, synth):
         d = Device(w, torch, qsa)
         wall, per = time_steps(d, 20, 5, torch)
         rep, mean = kernel_report(d, per)
+        b2b = back_to_back_us(d, torch)
+        cold, floor = cold_step_us(d, torch)
+        alg = d.pool_bytes() + d.prep_bytes() + d.score_bytes() + d.select_bytes()
         out[key] = {"rows": d.rows, "tokens": d.T, "pairs": d.pairs,
-                    "select_mask_us_per_row": round(mean["select"] / d.rows, 3),
+                    "select_mask_us_per_row": round(b2b["select"] / d.rows, 3),
                     "step_us_events": round(sum(mean.values()), 2),
-                    "pairs_per_s": round(d.pairs / (sum(mean.values()) * 1e-6), 1),
+                    "step_us_back_to_back": round(sum(b2b.values()), 2),
+                    "step_us_cold": cold,
+                    "event_pair_floor_us": floor,
+                    "alg_bytes_step": alg,
+                    "hbm_frac_back_to_back": round(alg / (sum(b2b.values()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "hbm_frac_cold_step": round(alg / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "pairs_per_s": round(d.pairs / (sum(b2b.values()) * 1e-6), 1),
+                    "kernels_back_to_back_us": b2b,
                     "kernels": rep}
         del d
         torch.cuda.empty_cache()
