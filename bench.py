@@ -41,6 +41,13 @@ def parse():
     ap.add_argument("--no-side", action="store_true", help="skip the decode and one-row figures")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU-oracle budget for the baseline sample")
+    ap.add_argument("--only", default=None,
+                    help="counter pass: run these comma-separated stages (pool,prep,score,select) "
+                         "--reps times each on --workload, after a plain copy of a known size")
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 counter runs of --only (FETCH_SIZE, then "
+                         "WRITE_SIZE) into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -213,26 +220,118 @@ def kernel_report(d: Device, per_us):
     return rep, mean
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the sources each stage's kernel is built from: its counters go stale when they change
+STAGE_SOURCES = {
+    "pool": ["pool.hip", "qsa_device.h"],
+    "prep": ["prep.hip", "qsa_device.h"],
+    "score": ["score.hip", "qsa_device.h"],
+    "select": ["select.hip", "qsa_device.h"],
+}
+# kernel-name fragment of each stage in rocprofv3 output
+STAGE_KERNELS = {"pool": "pool_kernel", "prep": "prep_kernel", "score": "score_mfma_kernel",
+                 "select": "select_kernel"}
+COPY_BYTES = 512 << 20  # the counter pass's calibration copy
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
-    kernel's source is unchanged since they were taken; else None."""
+def source_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for name in STAGE_SOURCES[stage]:
+        with open(os.path.join(ROOT, "sparse_attention_token_qsa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(stage: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
+    stage's sources are unchanged since the counters were taken; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         table = json.load(f)
-    entry = table.get(f"{kernel}:{workload}")
-    if not entry:
-        return None
-    src = os.path.join(ROOT, "sparse_attention_token_qsa_amd", "csrc", entry["source"])
-    if not os.path.exists(src) or source_hash(src) != entry["source_sha"]:
+    entry = table.get(f"{stage}:{workload}")
+    if not entry or entry.get("source_sha") != source_hash(stage):
         return None
     return entry["hbm_bytes_per_launch"]
+
+
+def counter_pass(args, torch, qsa, synth):
+    """Counter pass for rocprofv3 --pmc: one whole step so every stage's inputs
+    are in place, a plain device-to-device copy of COPY_BYTES run --reps times
+    (the calibration of the byte counters), then each --only stage --reps
+    times."""
+    w = synth.make_workload(args.workload)
+    d = Device(w, torch, qsa)
+    d.pool(); d.prep(); d.score(); d.select()
+    src = torch.full((COPY_BYTES,), 1, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    fns = {"pool": d.pool, "prep": d.prep, "score": d.score, "select": d.select}
+    stages = [s for s in args.only.split(",") if s]
+    for st in stages:
+        for _ in range(args.reps):
+            fns[st]()
+        torch.cuda.synchronize()
+    print(json.dumps({"counter_pass": w["name"], "stages": stages, "reps": args.reps,
+                      "copy_bytes": COPY_BYTES, "status": qsa.check_status(d.status)}))
+
+
+def _counter_rows(run_dir: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    return rows
+
+
+def traffic_table(fetch_dir: str, write_dir: str, workload: int):
+    """profiles/traffic.json from two counter passes: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) of each stage's kernel, each scaled by bytes / counter of
+    the calibration copy (the largest device-to-device copy dispatches), medians
+    over the dispatches."""
+    import synth
+    name = synth.WORKLOADS[workload]["name"]
+    out_path = os.path.join(ROOT, "profiles", "traffic.json")
+    table = {}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            table = json.load(f)
+    per = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(run_dir, counter)
+        copies = [v for _, k, v in rows if "copyBuffer" in k]
+        top = max(copies)
+        cal = median([v for v in copies if v >= 0.5 * top])
+        factor = COPY_BYTES / cal  # bytes per counter unit
+        for st, frag in STAGE_KERNELS.items():
+            vals = [v for _, k, v in rows if frag in k]
+            if vals:
+                per.setdefault(st, {})[counter] = (median(vals), factor, len(vals))
+    for st, c in per.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fk, ff, n1 = c["FETCH_SIZE"]
+        wk, wf, n2 = c["WRITE_SIZE"]
+        rd, wr = fk * ff, wk * wf
+        table[f"{st}:{name}"] = {
+            "kernel": STAGE_KERNELS[st], "fetch_kib": fk, "write_kib": wk,
+            "fetch_bytes_per_unit": round(ff, 2), "write_bytes_per_unit": round(wf, 2),
+            "dispatches": [n1, n2], "read_bytes": round(rd), "write_bytes": round(wr),
+            "hbm_bytes_per_launch": round(rd + wr), "source_sha": source_hash(st)}
+    with open(out_path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in table.items()}))
 
 
 # ----------------------------------------------------------------------------
@@ -320,6 +419,9 @@ def side_figures(torch, qsa, synth):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_table(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the indexer path here "
               f"is a single-GPU kernel set with no cross-GPU sharding.", file=sys.stderr)
@@ -329,6 +431,9 @@ def main():
     import synth
 
     qsa.load()
+    if args.only:
+        counter_pass(args, torch, qsa, synth)
+        return
     w = synth.make_workload(args.workload)
     d = Device(w, torch, qsa)
     wall, per = time_steps(d, args.steps, args.warmup, torch)
