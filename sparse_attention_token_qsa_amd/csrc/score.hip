@@ -461,6 +461,300 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
+
+// ---------------------------------------------------------------------------
+// Ring scorer for prepared queries and long row batches (prefill).
+//
+// 128 query rows per workgroup: wave w holds rows 32 w .. 32 w + 31 as four
+// 32 x 128 A-fragment sets (MS = 4) for the whole block loop.  Each step
+// takes one 32-block tile: the pooled keys stream through a D-stage LDS ring
+// filled by buffer loads straight to LDS (blocks at or past the workgroup's
+// longest prefix read as zeros and are never stored), and every wave reads
+// the tile's eight B fragments once and feeds each to four MFMAs.
+//
+// Two details keep the ring pipelined.  The B-fragment reads are inline
+// assembly: a compiler-visible LDS read behind an in-flight load to LDS makes
+// the compiler drain every outstanding memory operation first, scores
+// included.  And each step waits with vmcnt for exactly the next tile's
+// loads: a wave's loads and score stores retire in issue order, and the
+// stores issued since that tile's loads are counted (at most 63).
+//
+// Epilogue: phase A runs acc[0..1]'s MFMAs and stores the previous step's
+// acc[2..3] scores; phase B runs acc[2..3]'s MFMAs and stores acc[0..1]'s,
+// so relu / head sum / scale of one pair overlaps the other pair's MFMAs.
+// ---------------------------------------------------------------------------
+
+constexpr int kRingRows = 128;  // query rows per workgroup
+constexpr int kRingTile = 32;   // blocks per step
+constexpr int kRingStages = 4;
+
+struct RingArgs {
+  const uint16_t* qhat;
+  const int32_t* pos;
+  int64_t rows;
+  const uint16_t* pooled;
+  int64_t tokens;
+  float* scores;
+  int64_t score_cols;
+  int32_t* status;
+  int splits;  // workgroups per row group; split s takes tiles s, s + splits, ...
+  int tasks;
+};
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+// One 16-byte LDS read as inline assembly (see above); the value may only be
+// used after lds_wait8.
+template <int OFF>
+__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+// Waits for this wave's LDS reads; the fragments become usable after it.
+__device__ __forceinline__ void lds_wait8(bf16x8_t (&b)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7])
+               :
+               : "memory");
+}
+// One LDS word read and its wait, as inline assembly.
+__device__ __forceinline__ int lds_read_word(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+// Score of query row (q4 of the lane's accumulator rows) from its four head
+// dot products: relu(d) = (d + |d|) / 2 exactly (NaN stays NaN), so the head
+// sum of the doubled terms times scale / 2 is the f32 score.
+__device__ __forceinline__ float pair_score(const f32x16_t& acc, int q4) {
+  const float h0 = acc[4 * q4 + 0], h1 = acc[4 * q4 + 1];
+  const float h2 = acc[4 * q4 + 2], h3 = acc[4 * q4 + 3];
+  float s = (h0 + fabsf(h0)) + (h1 + fabsf(h1));
+  s = s + (h2 + fabsf(h2));
+  s = s + (h3 + fabsf(h3));
+  return s * (0.5f * kScale);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
+  constexpr int RG = kRingRows, TILE = kRingTile, STAGE = TILE * 256;
+  constexpr int kL = 2;        // 1 KiB ring loads per wave per tile
+  constexpr int kStores = 16;  // score stores per wave per step
+  __shared__ __attribute__((aligned(16))) unsigned char ring[D * STAGE];
+  __shared__ int nvis[RG];
+  __shared__ int sh_nmax, sh_nmin;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // consecutive tasks (the splits of one row group) share an XCD, so their
+  // neighbouring pieces of the same score rows meet in one L2
+  int task = blockIdx.x;
+  {
+    const int per = a.tasks >> 3;
+    if (task < (per << 3)) task = (task & 7) * per + (task >> 3);
+  }
+  const int rg = task / a.splits;
+  const int split = task - rg * a.splits;
+  const int64_t row0 = static_cast<int64_t>(rg) * RG;
+  const int blk_begin = split * TILE;
+  const int stride = a.splits * TILE;
+
+  // A fragments: subtile ms of wave w = rows 32 w + 8 ms .. + 7 as 32 M-rows (row, head)
+  bf16x8_t afrag[4][8];
+  {
+    const int khalf = 8 * (lane >> 5);
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      int64_t rr = row0 + 32 * wave + 8 * ms + ((lane & 31) >> 2);
+      rr = rr < a.rows ? rr : a.rows - 1;  // rows past the end are never stored
+      const uint16_t* src = a.qhat + rr * (kHeads * kHeadDim) + kHeadDim * (lane & 3) + khalf;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) afrag[ms][ks] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ks);
+    }
+  }
+  // visible block counts (wave 0, lane l: rows l and l + 64)
+  if (wave == 0) {
+    uint32_t mx = 0u, mn = 0x7FFFFFFFu;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int lr = lane + 64 * hh;
+      int n = 0;
+      const int64_t r = row0 + lr;
+      if (r < a.rows) {
+        const int p = a.pos[r];
+        if (p >= 0 && p < a.tokens)
+          n = (p + 1) / kRatio;
+        else if (split == 0)
+          atomicOr(a.status, 1);
+      }
+      nvis[lr] = n;
+      mx = max(mx, static_cast<uint32_t>(n));
+      mn = min(mn, static_cast<uint32_t>(n));
+    }
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
+    if (lane == 0) {
+      sh_nmax = static_cast<int>(mx);
+      sh_nmin = static_cast<int>(mn);
+    }
+  }
+  __syncthreads();
+  const int nmax = sh_nmax;
+  const int nmin = sh_nmin;  // blocks every row of the workgroup sees
+  if (blk_begin >= nmax) return;  // uniform; nothing in flight
+
+  // ---- key ring.  Load i of wave w fills tile rows 4 (2 w + i) + lane / 16
+  // with the key's 16-byte chunk (lane % 16) ^ (row & 7) at chunk lane % 16,
+  // so a B-fragment read (32 rows, one chunk each) spreads over all banks.
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.pooled), static_cast<short>(0), nmax * 256, 0x00020000);
+  const int lrow = lane >> 4, lchunk = lane & 15;
+  auto load_tile = [&](int nb0, int stage) {
+#pragma unroll
+    for (int i = 0; i < kL; ++i) {
+      const int row = 4 * (wave * kL + i) + lrow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krsrc, (__attribute__((address_space(3))) void*)(ring + stage * STAGE + 1024 * (wave * kL + i)), 16,
+          row * 256 + 16 * (lchunk ^ (row & 7)), nb0 * 256, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t);
+
+  // B fragment ks of lane (r, h): stage row r, logical chunk 2 ks + h at
+  // chunk (2 ks + h) ^ (r & 7) = 2 ((ks & 3) ^ s2) + (h ^ s1) + 8 (ks >> 2).
+  const int r = lane & 31, h = lane >> 5;
+  const int s2 = (r & 7) >> 1, s1 = r & 1;
+  const uint32_t bbase = lds_addr(ring) + r * 256 + 16 * (h ^ s1);
+  const uint32_t s2x = 32 * s2;
+  const uint32_t nvis_lane = lds_addr(nvis) + 4 * (32 * wave + h);
+
+  // score stores through a resource over the group's rows: lane (r, h) of
+  // subtile ms writes row 32 w + 8 ms + 2 q4 + h, column nb0 + r.  An offset
+  // past the resource drops the store (blocks outside a row's prefix).
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores + row0 * a.score_cols, static_cast<short>(0), static_cast<int>(RG * a.score_cols * 4), 0x00020000);
+  const int vbase = ((32 * wave + h) * static_cast<int>(a.score_cols) + r) * 4;
+  const int rowbytes = static_cast<int>(a.score_cols) * 4;
+  constexpr int kDrop = static_cast<int>(0x80000000u);
+
+  auto pair_store = [&](const f32x16_t& x0, const f32x16_t& x1, int m0, int nb0, bool live, bool fast) {
+    float sc[8];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      sc[q4] = pair_score(x0, q4);
+      sc[4 + q4] = pair_score(x1, q4);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ms = m0 + (j >> 2), q4 = j & 3;
+      int off = vbase;
+      if (!fast) {
+        const int nv = lds_read_word(nvis_lane + 4 * (8 * ms + 2 * q4));
+        off = (live && nb0 + r < nv) ? vbase : kDrop;
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[j]), orsrc, off,
+                                            (8 * ms + 2 * q4) * rowbytes + 4 * nb0, 0);
+    }
+  };
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[ms][v] = 0.0f;
+
+  wait_vmcnt<(D - 2) * kL>();  // tile 0 landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  int stage = 0, step = 0;
+  int prev_nb0 = blk_begin;
+  for (int nb0 = blk_begin; nb0 < nmax; nb0 += stride) {
+    int lstage = stage + D - 1;
+    lstage = lstage >= D ? lstage - D : lstage;
+    load_tile(nb0 + (D - 1) * stride, lstage);
+    bf16x8_t bf[8];
+    {
+      const uint32_t bb = bbase + stage * STAGE;
+      const uint32_t b0 = bb + s2x, b1 = bb + (32u ^ s2x), b2 = bb + (64u ^ s2x), b3 = bb + (96u ^ s2x);
+      bf[0] = lds_read16<0>(b0);
+      bf[1] = lds_read16<0>(b1);
+      bf[2] = lds_read16<0>(b2);
+      bf[3] = lds_read16<0>(b3);
+      bf[4] = lds_read16<128>(b0);
+      bf[5] = lds_read16<128>(b1);
+      bf[6] = lds_read16<128>(b2);
+      bf[7] = lds_read16<128>(b3);
+    }
+    // phase A: the previous step's acc[2..3] (dropped in the first step)
+    pair_store(acc[2], acc[3], 2, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin);
+    lds_wait8(bf);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[0][ks], bf[ks], ks ? acc[0] : f32x16_t{}, 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[1][ks], bf[ks], ks ? acc[1] : f32x16_t{}, 0, 0, 0);
+    }
+    // phase B: this step's acc[0..1]
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
+    }
+    pair_store(acc[0], acc[1], 0, nb0, true, nb0 + TILE <= nmin);
+    // Tile t + 1 has landed once at most N of this wave's memory operations
+    // are outstanding, N = what was issued after its loads: the loads of
+    // (D - 2) tiles and the 16 stores of each step since (D - 1 steps in the
+    // steady state, step + 1 in the first D - 2 steps).
+    {
+      constexpr int NA0 = (D - 2) * kL + (D - 1) * kStores;
+      constexpr int NA = NA0 > 63 ? 63 : NA0;
+      constexpr int N0 = (D - 2) * kL + kStores;
+      constexpr int N1 = (D - 2) * kL + 2 * kStores;
+      constexpr int N2 = (D - 2) * kL + 3 * kStores;
+      static_assert(D <= 5, "steps before the steady state: at most three");
+      if (step >= D - 2) wait_vmcnt<NA>();
+      else if (step == 0) wait_vmcnt<(N0 > 63 ? 63 : N0)>();
+      else if (step == 1) wait_vmcnt<(N1 > 63 ? 63 : N1)>();
+      else wait_vmcnt<(N2 > 63 ? 63 : N2)>();
+    }
+    __builtin_amdgcn_s_barrier();  // the stage read this step may be refilled
+    asm volatile("" ::: "memory");
+    prev_nb0 = nb0;
+    ++step;
+    stage = stage + 1 == D ? 0 : stage + 1;
+  }
+  pair_store(acc[2], acc[3], 2, prev_nb0, true, prev_nb0 + TILE <= nmin);
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+}
+
+hipError_t launch_score_ring(const ScoreArgs& base, hipStream_t stream) {
+  RingArgs a{};
+  a.qhat = base.qhat;
+  a.pos = base.pos;
+  a.rows = base.rows;
+  a.pooled = base.pooled;
+  a.tokens = base.tokens;
+  a.scores = base.scores;
+  a.score_cols = base.score_cols;
+  a.status = base.status;
+  const int64_t nb_total = a.tokens / kRatio;
+  const int64_t row_groups = (a.rows + kRingRows - 1) / kRingRows;
+  int64_t n_tiles = (nb_total + kRingTile - 1) / kRingTile;
+  if (n_tiles < 1) n_tiles = 1;
+  int64_t splits = (1024 + row_groups - 1) / row_groups;
+  if (splits < 1) splits = 1;
+  if (splits > n_tiles) splits = n_tiles;
+  if (row_groups * splits > 0x7FFFFFFF) return hipErrorInvalidValue;
+  a.splits = static_cast<int>(splits);
+  a.tasks = static_cast<int>(row_groups * splits);
+  score_ring_kernel<kRingStages><<<dim3(static_cast<unsigned>(a.tasks)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int WM, int MS, int D, bool PREP>
 hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
   using G = ScoreGeom<WM, MS, D, PREP>;
@@ -492,6 +786,10 @@ hipError_t launch_score_rows(const ScoreArgs& a, hipStream_t stream) {
   // Prepared queries: 32 rows per wave when there are enough rows, so each
   // B fragment feeds four MFMAs.  The one-call path keeps 8 rows per wave,
   // which bounds its query-prep LDS.
+  // Prepared queries, long batches: the ring scorer (its store resource
+  // spans 128 rows of scores, within 2^31 bytes).
+  if constexpr (PREP)
+    if (a.rows >= kRingRows && a.score_cols <= 0x7FFFFFFF / (4 * kRingRows)) return launch_score_ring(a, stream);
   if constexpr (PREP)
     if (a.rows >= 64) return launch_score_geom<2, 4, 4, PREP>(a, stream);
   if (a.rows >= 32) return launch_score_geom<4, 1, 4, PREP>(a, stream);

@@ -279,6 +279,54 @@ def test_score_nan_key_and_bad_positions(path):
             assert np.all(np.isfinite(got[r, :n]))
 
 
+def test_score_long_batches_ragged_rows_bad_positions_nan_key():
+    """The prepared-query scorer on batches of 128 rows and more (the shape
+    prefill uses): a row count that is not a multiple of 128, ragged prefixes
+    from position 0 to the last token, out-of-range positions, a NaN key and
+    spare score columns.  Valid rows match the oracle within the bound, the
+    NaN key poisons exactly block 50 of the rows that see it, nothing is
+    written outside a row's prefix, and the scores equal the one-call
+    scorer's bit for bit."""
+    w = workload(2)
+    T = w["tokens"]
+    rng = np.random.default_rng(77)
+    R = 301
+    pos = rng.integers(0, T, size=R).astype(np.int32)
+    pos[:6] = [0, 3, 4, T - 1, T - 2, 203]
+    pos[[10, 150, 300]] = [-1, T, 1 << 30]
+    q = w["queries"][rng.choice(len(w["pos"]), size=R, replace=False)]
+    pooled = oracle_pooled(2).copy()
+    pooled[50] = 0x7FC0
+    cols = T // 4 + 3
+    sentinel = np.float32(-7.25)
+    note(f"score long batch: {R} rows over {T} tokens, score_cols {cols}")
+    got, st = gpu_scores_prepped(w, u16_dev(pooled), pos=pos, q=q, score_cols=cols, sentinel=sentinel)
+    assert st == O.STATUS_BAD_POSITION
+    ref, st2 = gpu_scores(w, u16_dev(pooled), pos=pos, q=q, score_cols=cols, sentinel=sentinel)
+    assert st2 == O.STATUS_BAD_POSITION
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    valid = (pos >= 0) & (pos < T)
+    assert np.all(got[~valid] == sentinel)
+    vrows = np.nonzero(valid)[0]
+    qhat = O.prep_queries(q[vrows], pos[vrows], w["q_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    want = O.score_rows(qhat, pos[vrows], pooled, T)
+    worst = 0.0
+    for i, r in enumerate(vrows):
+        s = want[i]
+        n = len(s)
+        assert np.all(got[r, n:] == sentinel), "wrote past the visible prefix"
+        if n > 50:
+            assert np.isnan(got[r, 50]) and np.isnan(s[50])
+            s = np.delete(s, 50)
+            g = np.delete(got[r, :n], 50)
+        else:
+            g = got[r, :n]
+        if len(s):
+            worst = max(worst, float(np.max(np.abs(g.astype(np.float64) - s))))
+    note(f"  max |gpu - oracle| = {worst:.3e}")
+    assert worst <= SCORE_ATOL
+
+
 # ------------------------------------------------------------ end to end ----
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
