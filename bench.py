@@ -2,7 +2,8 @@
 """Benchmark of the QSA indexer hot path on one MI355X.
 
 One step = qsa_pool_keys (every block) -> qsa_prep_queries (every row) ->
-qsa_score_prepped (every row) -> qsa_select_mask (every row) over one batch
+qsa_score_prepped (every row) -> qsa_select_mask_ws (every row; few long
+rows split over workgroups through a workspace allocated once) over one batch
 of a seeded synthetic workload,
 inputs resident in HBM.  W untimed warm-up steps, then K timed steps between
 two device synchronisations; per-kernel durations come from HIP events
@@ -73,6 +74,8 @@ class Device:
         self.scores = torch.empty(rows * max(self.cols, 1), dtype=torch.float32, device=dev)
         self.mask = torch.empty((rows, T), dtype=torch.uint8, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        ws = qsa.qsa_select_workspace_bytes(rows, T)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
         n = (w["pos"].astype(np_.int64) + 1) // 4
         self.pairs = int(n.sum())
         self.nmax = int(n.max())
@@ -91,8 +94,8 @@ class Device:
                                    self.status)
 
     def select(self):
-        self.qsa.qsa_select_mask(self.scores, self.cols, self.pos, self.T, self.w["budget"],
-                                 self.mask, self.status)
+        self.qsa.qsa_select_mask_ws(self.scores, self.cols, self.pos, self.T, self.w["budget"],
+                                    self.mask, self.status, self.ws)
 
     # algorithmic bytes / flops per launch
     def pool_bytes(self):

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -178,6 +178,39 @@ int qsa_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
 int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
                     const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
                     uint8_t* mask, int32_t* dev_status, void* stream);
+
+/*
+ * qsa_select_workspace_bytes -- device workspace qsa_select_mask_ws needs for
+ * `rows` rows over a `tokens`-token cache: 0 when it selects one workgroup
+ * per row (more than 128 rows, or caches of at most 65536 + 3 tokens), else
+ * 4352 bytes per 16384 tokens (rounded up) per row.  Negative QSA_ERR_EXTENT /
+ * QSA_ERR_CAPACITY for negative extents or tokens > QSA_MAX_TOKENS.
+ */
+int64_t qsa_select_workspace_bytes(int64_t rows, int64_t tokens);
+
+/*
+ * qsa_select_mask_ws -- qsa_select_mask, same kept sets and mask bytes, for
+ * batches of few long rows (decode).  [SEL] "Exact semantics" as for
+ * qsa_select_mask.  When qsa_select_workspace_bytes(rows, tokens) > 0 each
+ * row is split into chunks of 4096 blocks: one kernel emits every chunk's
+ * exact local top-(budget/4) into the workspace (the row's kept blocks are
+ * among them), a second finds the row's cut from that union and writes the
+ * mask, one 16384-token slice per workgroup.  Otherwise it runs the
+ * one-workgroup-per-row kernel of qsa_select_mask and ignores the workspace.
+ *
+ *   workspace        device memory owned by the caller, 16-byte aligned, at
+ *                    least workspace_bytes >= qsa_select_workspace_bytes(rows,
+ *                    tokens) long; its contents on entry do not matter and
+ *                    on return are unspecified.  Two calls in flight on the
+ *                    same workspace race.
+ * Refusals: those of qsa_select_mask; QSA_ERR_NULL (workspace NULL when
+ * needed), QSA_ERR_CAPACITY (workspace_bytes too small), QSA_ERR_EXTENT
+ * (workspace_bytes < 0), QSA_ERR_PARAM (workspace not 16-byte aligned).
+ */
+int qsa_select_mask_ws(const float* scores, int64_t score_cols, int64_t scores_len,
+                       const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                       uint8_t* mask, int32_t* dev_status, void* workspace,
+                       int64_t workspace_bytes, void* stream);
 
 /*
  * qsa_rope_inv_freq -- host only: the rotary frequencies the kernels use,

@@ -18,7 +18,8 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
                    strerror)
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
-           "qsa_select_mask", "qsa_rope_inv_freq",
+           "qsa_select_mask", "qsa_select_workspace_bytes", "qsa_select_mask_ws",
+           "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
@@ -170,6 +171,39 @@ def qsa_select_mask(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, to
     _check(lib.qsa_select_mask(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
                                budget, _ptr(mask), _ptr(dev_status), _stream_ptr(stream)),
            "qsa_select_mask")
+
+
+def qsa_select_workspace_bytes(rows: int, tokens: int) -> int:
+    """Device workspace bytes qsa_select_mask_ws needs (0: none)."""
+    n = load().qsa_select_workspace_bytes(rows, tokens)
+    if n < 0:
+        raise QsaError(int(n), "qsa_select_workspace_bytes")
+    return int(n)
+
+
+def qsa_select_mask_ws(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, tokens: int,
+                       budget: int, mask: torch.Tensor, dev_status: torch.Tensor,
+                       workspace: torch.Tensor | None, stream=None) -> None:
+    """qsa_select_mask for few long rows, split over workgroups; `workspace`
+    is a device tensor of at least qsa_select_workspace_bytes(rows, tokens)
+    bytes (may be None when that is 0)."""
+    _dev(scores, "scores", (torch.float32,))
+    _dev(pos, "pos", (torch.int32,))
+    _dev(mask, "mask", (torch.uint8,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous(), "pos must be contiguous")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    _need(mask.is_contiguous() and mask.numel() >= rows * tokens, "mask must be contiguous [rows, tokens]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    _check(lib.qsa_select_mask_ws(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
+                                  budget, _ptr(mask), _ptr(dev_status), _ptr(workspace), ws_bytes,
+                                  _stream_ptr(stream)), "qsa_select_mask_ws")
 
 
 def qsa_rope_inv_freq(rotary_dim: int, rope_theta: float) -> list:

@@ -147,9 +147,9 @@ int qsa_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
                                                  static_cast<hipStream_t>(stream)));
 }
 
-int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
-                    const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
-                    uint8_t* mask, int32_t* dev_status, void* stream) {
+namespace {
+int check_select(const float* scores, int64_t score_cols, int64_t scores_len, const int32_t* pos,
+                 int64_t rows, int64_t tokens, int64_t budget, uint8_t* mask, int32_t* dev_status) {
   if (rows < 0 || tokens < 0 || score_cols < 0 || scores_len < 0) return QSA_ERR_EXTENT;
   if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
     return QSA_ERR_BUDGET;
@@ -162,9 +162,43 @@ int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
   if (rows == 0 || tokens == 0) return QSA_OK;
   if (pos == nullptr || mask == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
   if (tokens >= QSA_RATIO && scores == nullptr) return QSA_ERR_NULL;
+  return 1;  // valid and not empty
+}
+}  // namespace
+
+int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
+                    const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                    uint8_t* mask, int32_t* dev_status, void* stream) {
+  const int rc = check_select(scores, score_cols, scores_len, pos, rows, tokens, budget, mask, dev_status);
+  if (rc <= 0) return rc;
   return launch_status(qsa::launch_select(scores, score_cols, pos, rows, tokens,
                                           static_cast<int>(budget / QSA_RATIO), mask,
                                           dev_status, static_cast<hipStream_t>(stream)));
+}
+
+int64_t qsa_select_workspace_bytes(int64_t rows, int64_t tokens) {
+  if (rows < 0 || tokens < 0) return QSA_ERR_EXTENT;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (rows == 0 || tokens == 0 || !qsa::select_split_pays(rows, tokens)) return 0;
+  return qsa::select_split_workspace_bytes(rows, tokens);
+}
+
+int qsa_select_mask_ws(const float* scores, int64_t score_cols, int64_t scores_len,
+                       const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                       uint8_t* mask, int32_t* dev_status, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  const int rc = check_select(scores, score_cols, scores_len, pos, rows, tokens, budget, mask, dev_status);
+  if (rc <= 0) return rc;
+  if (workspace_bytes < 0) return QSA_ERR_EXTENT;
+  const int keep_max = static_cast<int>(budget / QSA_RATIO);
+  if (!qsa::select_split_pays(rows, tokens))
+    return launch_status(qsa::launch_select(scores, score_cols, pos, rows, tokens, keep_max, mask,
+                                            dev_status, static_cast<hipStream_t>(stream)));
+  if (workspace == nullptr) return QSA_ERR_NULL;
+  if (workspace_bytes < qsa::select_split_workspace_bytes(rows, tokens)) return QSA_ERR_CAPACITY;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return QSA_ERR_PARAM;
+  return launch_status(qsa::launch_select_split(scores, score_cols, pos, rows, tokens, keep_max, mask,
+                                                dev_status, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -34,4 +34,12 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
                          int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                          int32_t* status, hipStream_t stream);
 
+// Split select for few long rows (select_split.hip): two launches over a
+// caller-provided workspace of select_split_workspace_bytes(rows, tokens).
+bool select_split_pays(int64_t rows, int64_t tokens);
+int64_t select_split_workspace_bytes(int64_t rows, int64_t tokens);
+hipError_t launch_select_split(const float* scores, int64_t score_cols, const int32_t* pos,
+                               int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
+                               int32_t* status, void* workspace, hipStream_t stream);
+
 }  // namespace qsa

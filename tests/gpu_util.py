@@ -108,3 +108,16 @@ def gpu_select(scores: np.ndarray, cols: int, pos, tokens: int, budget: int):
     qsa.qsa_select_mask(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, mask, st)
     s = qsa.check_status(st)
     return mask.cpu().numpy(), s
+
+
+def gpu_select_ws(scores: np.ndarray, cols: int, pos, tokens: int, budget: int, fill: int = 0x5A):
+    """qsa_select_mask_ws with a workspace of exactly the reported size,
+    prefilled with junk (its contents on entry must not matter)."""
+    rows = len(pos)
+    mask = torch.full((rows, tokens), 0xAB, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    nbytes = qsa.qsa_select_workspace_bytes(rows, tokens)
+    ws = torch.full((max(nbytes, 16),), fill, dtype=torch.uint8, device=DEV) if nbytes else None
+    qsa.qsa_select_mask_ws(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, mask, st, ws)
+    s = qsa.check_status(st)
+    return mask.cpu().numpy(), s, nbytes

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 2
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 3
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -148,6 +148,45 @@ def test_select_refusals(lib):
     assert select(lib, scores_len=127) == CAP
     assert select(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
     assert select(lib, rows=2**40, score_cols=16, scores_len=2**62) == CAP
+
+
+def select_ws(lib, **kw):
+    a = dict(scores=P, score_cols=16385, scores_len=8 * 16385, pos=P, rows=8, tokens=65540,
+             budget=2048, mask=P, status=P, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.qsa_select_mask_ws(a["scores"], a["score_cols"], a["scores_len"], a["pos"], a["rows"],
+                                  a["tokens"], a["budget"], a["mask"], a["status"], a["ws"],
+                                  a["ws_bytes"], None)
+
+
+def test_select_workspace_sizes(lib):
+    # one workgroup per row: no workspace
+    assert lib.qsa_select_workspace_bytes(8192, 65536) == 0
+    assert lib.qsa_select_workspace_bytes(8, 16384) == 0
+    assert lib.qsa_select_workspace_bytes(0, 65536) == 0
+    # few long rows: one list of 512 composites per 16384-token slice, plus counts
+    assert lib.qsa_select_workspace_bytes(16, 262144) == 16 * 16 * (4096 + 256)
+    assert lib.qsa_select_workspace_bytes(1, 262147) == 17 * (4096 + 256)
+    assert lib.qsa_select_workspace_bytes(64, 65536) == 0
+    assert lib.qsa_select_workspace_bytes(64, 65540) == 64 * 5 * (4096 + 256)
+    assert lib.qsa_select_workspace_bytes(129, 262144) == 0
+    assert lib.qsa_select_workspace_bytes(-1, 64) == EXTENT
+    assert lib.qsa_select_workspace_bytes(8, 262148) == CAP
+
+
+def test_select_ws_refusals(lib):
+    assert select_ws(lib, rows=0) == OK
+    assert select_ws(lib, tokens=0, score_cols=0) == OK
+    for k in ("scores", "pos", "mask", "status", "ws"):
+        assert select_ws(lib, **{k: None}) == NULL, k
+    assert select_ws(lib, rows=-1) == EXTENT
+    assert select_ws(lib, ws_bytes=-1) == EXTENT
+    for b in (0, -4, 2, 2052):
+        assert select_ws(lib, budget=b) == BUDGET, b
+    assert select_ws(lib, score_cols=16384) == STRIDE
+    assert select_ws(lib, scores_len=8 * 16385 - 1) == CAP
+    assert select_ws(lib, ws_bytes=8 * 5 * (4096 + 256) - 1) == CAP
+    assert select_ws(lib, ws=P + 8) == PARAM
 
 
 def prep(lib, **kw):

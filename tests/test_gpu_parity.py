@@ -15,7 +15,7 @@ import torch
 import oracle as O
 import synth
 from tests.gpu_util import (DEV, gpu_pool, gpu_prep, gpu_scores, gpu_scores_prepped, gpu_select,
-                            note, u16_dev, u16_host, workload)
+                            gpu_select_ws, note, u16_dev, u16_host, workload)
 from tests.test_oracle_pins import check_structure
 
 pytestmark = pytest.mark.gpu
@@ -208,6 +208,114 @@ def test_select_longest_supported_row():
         want, _ = O.select_mask(scores, cols, pos2, T, 2048)
         got, st = gpu_select(scores, cols, pos2, T, 2048)
         assert st == 0 and np.array_equal(got, want)
+
+
+# ------------------------------------------------- select, split rows ----
+
+@pytest.mark.parametrize("wid", [3, 4])
+def test_select_ws_on_oracle_scores_bit_exact(wid):
+    """Decode batches through the split selector: the oracle's scores of
+    every sampled row, masks equal to the oracle's byte for byte."""
+    w = workload(wid)
+    rows = sample_rows(wid)
+    T = w["tokens"]
+    cols = T // 4
+    sc = dense(oracle_scores(wid, rows), cols)
+    pos = w["pos"][rows]
+    note(f"split select on oracle scores: workload {wid}, {len(rows)} rows")
+    want, wst = O.select_mask(sc, cols, pos, T, w["budget"])
+    got, gst, nbytes = gpu_select_ws(sc, cols, pos, T, w["budget"])
+    assert (nbytes > 0) == (T > 65539), "the split path runs on caches past 64k tokens"
+    assert gst == wst == 0
+    bad = [r for r in range(len(rows)) if not np.array_equal(got[r], want[r])]
+    assert not bad, (bad[:5], pos[bad[:5]])
+
+
+@pytest.mark.parametrize("kind", ["zeros", "ties", "lowbyte", "wild", "equal", "random", "poison"])
+def test_select_ws_fixtures_bit_exact(kind):
+    scores, cols, pos, T = synth.selector_fixture(kind)
+    note(f"split select fixture {kind}: rows {len(pos)}, tokens {T}")
+    for budget in (2048, 64, 4):
+        want, wst = O.select_mask(scores, cols, pos, T, budget)
+        got, gst, nbytes = gpu_select_ws(scores, cols, pos, T, budget)
+        assert nbytes > 0
+        assert gst == wst
+        bad = [r for r in range(len(pos)) if not np.array_equal(got[r], want[r])]
+        assert not bad, (budget, bad[:5], pos[bad[:5]])
+
+
+def test_select_ws_kept_blocks_in_one_chunk_and_across_boundaries():
+    """Kept sets that sit in one 4096-block chunk (rising scores: the last
+    chunk; all equal: the first 512 indices), ties straddling a chunk
+    boundary, and a single kept block."""
+    T = 65536 + 4 * 4096 + 7
+    n = T // 4
+    pos = np.array([T - 1, T - 2, 4 * 8192 + 3, 4 * 4096 - 1, 4 * 4096 + 3, T - 1], dtype=np.int32)
+    cols = n
+    sc = np.full((len(pos), cols), np.nan, np.float32)
+    nb = (pos.astype(np.int64) + 1) // 4
+    sc[0, : nb[0]] = np.arange(nb[0], dtype=np.float32)          # rising: last chunk
+    sc[1, : nb[1]] = 1.5                                          # all equal: lowest indices
+    v = np.zeros(nb[2], np.float32)
+    v[4096 - 300: 4096 + 300] = 2.0                               # 600 ties across a boundary
+    sc[2, : nb[2]] = v
+    rng = np.random.default_rng(5)
+    sc[3, : nb[3]] = rng.standard_normal(nb[3])                   # exactly one chunk
+    sc[4, : nb[4]] = rng.standard_normal(nb[4])                   # one chunk plus one block
+    sc[5, : nb[5]] = -np.arange(nb[5], dtype=np.float32)          # falling: first chunk
+    note(f"split select boundaries: tokens {T}")
+    for budget in (2048, 4):
+        want, wst = O.select_mask(sc, cols, pos, T, budget)
+        got, gst, nbytes = gpu_select_ws(sc, cols, pos, T, budget)
+        assert nbytes > 0 and gst == wst == 0
+        bad = [r for r in range(len(pos)) if not np.array_equal(got[r], want[r])]
+        assert not bad, (budget, bad)
+
+
+@pytest.mark.parametrize("T", [65541, 65554, 131075, 262147])
+def test_select_ws_ragged_tokens_spare_columns_bad_positions(T):
+    """Token counts off the 16-byte grid (byte-wise mask path), a score row
+    stride off the 4-float grid (scalar loads), out-of-range positions and a
+    non-finite score in one row."""
+    pos = np.array([T - 1, 0, 3, 4, 2051, T // 2, -1, T, 2 * T + 5, T - 3], dtype=np.int32)
+    cols = T // 4 + 3
+    scores = np.full((len(pos), cols), np.nan, np.float32)
+    rng = np.random.default_rng(T)
+    for r, p in enumerate(pos):
+        n = (int(p) + 1) // 4 if 0 <= p < T else 0
+        scores[r, :n] = rng.standard_normal(n)
+    scores[9, 17] = np.inf
+    note(f"split select ragged: tokens {T}")
+    want, wst = O.select_mask(scores, cols, pos, T, 2048)
+    got, gst, nbytes = gpu_select_ws(scores, cols, pos, T, 2048)
+    assert nbytes > 0
+    assert gst == wst == O.STATUS_BAD_POSITION | O.STATUS_NONFINITE_SCORE
+    assert np.array_equal(got, want)
+
+
+def test_select_ws_equals_select_and_reuses_its_workspace():
+    """Two calls in a row on one workspace (the second over shorter rows)
+    match qsa_select_mask bit for bit; many rows take the one-workgroup path
+    and need no workspace."""
+    w = workload(4)
+    T = w["tokens"]
+    cols = T // 4
+    rng = np.random.default_rng(11)
+    rows = 24
+    pos = np.sort(rng.integers(T // 2, T, size=rows)).astype(np.int32)
+    sc = rng.standard_normal((rows, cols)).astype(np.float32)
+    nbytes = __import__("sparse_attention_token_qsa_amd").qsa_select_workspace_bytes(rows, T)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    import sparse_attention_token_qsa_amd as qsa
+    from tests.gpu_util import f32_dev, i32_dev, status_word
+    for p2 in (pos, pos // 3):
+        mask = torch.full((rows, T), 0xAB, dtype=torch.uint8, device=DEV)
+        st = status_word()
+        qsa.qsa_select_mask_ws(f32_dev(sc.reshape(-1)), cols, i32_dev(p2), T, 2048, mask, st, ws)
+        assert qsa.check_status(st) == 0
+        ref, rst = gpu_select(sc, cols, p2, T, 2048)
+        assert rst == 0 and np.array_equal(mask.cpu().numpy(), ref)
+    assert qsa.qsa_select_workspace_bytes(4096, T) == 0
 
 
 # ----------------------------------------------------------------- score ----
