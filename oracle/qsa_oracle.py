@@ -319,6 +319,51 @@ def select_mask(scores: np.ndarray, score_cols: int, pos: np.ndarray, tokens: in
     return mask, status
 
 
+def select_indices_row(row_scores: np.ndarray, p: int, tokens: int, budget: int):
+    """One row's kept token indices (int32, ascending), padded with -1 to
+    budget + 3 entries, their count, and the status bits.
+
+    [QSA] decode_select: the kept blocks (the keep first under the canonical
+    order) are sorted ascending and each contributes its RATIO tokens
+    RATIO*b .. RATIO*b + RATIO - 1; the tail tokens RATIO*n .. p follow.
+    [SCORE] "Next: P3" bounds the list by budget + RATIO - 1 entries.
+    Refusals as in select_mask_row: count 0, all entries -1.
+    """
+    cap = budget + RATIO - 1
+    out = np.full(cap, -1, dtype=np.int32)
+    if p < 0 or p >= tokens:
+        return out, 0, STATUS_BAD_POSITION
+    n = visible_blocks(p)
+    s = np.asarray(row_scores[:n], dtype=np.float32)
+    if not np.all(np.isfinite(s)):
+        return out, 0, STATUS_NONFINITE_SCORE
+    keep = min(budget // RATIO, n)
+    sel = []
+    for b in kept_blocks(s, keep):
+        sel.extend(range(RATIO * int(b), RATIO * int(b) + RATIO))
+    sel.extend(range(RATIO * n, p + 1))
+    out[: len(sel)] = sel
+    return out, len(sel), 0
+
+
+def select_indices(scores: np.ndarray, score_cols: int, pos: np.ndarray, tokens: int,
+                   budget: int):
+    """Index lists of all rows from a row-major [rows, score_cols] f32 score
+    buffer.  Returns (idx [rows, budget + 3] int32, counts [rows] int32,
+    status bits OR-ed over rows)."""
+    check_budget(budget)
+    flat = np.asarray(scores, dtype=np.float32).reshape(-1)
+    rows = len(pos)
+    idx = np.full((rows, budget + RATIO - 1), -1, dtype=np.int32)
+    counts = np.zeros(rows, dtype=np.int32)
+    status = 0
+    for r in range(rows):
+        row = flat[r * score_cols: (r + 1) * score_cols]
+        idx[r], counts[r], st = select_indices_row(row, int(pos[r]), tokens, budget)
+        status |= st
+    return idx, counts, status
+
+
 # ----------------------------------------------------------------------------
 # Whole path
 # ----------------------------------------------------------------------------

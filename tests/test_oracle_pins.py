@@ -464,3 +464,81 @@ def test_mutation_controls_are_caught_by_the_invariants():
             check_structure(m, scores[r], int(pos[r]), T, 2048)
         caught += 1
     assert caught >= 15
+
+
+# ------------------------------------------------------------ index lists ----
+
+def check_index_list(idx_row, count, mask_row, p, budget):
+    """An index row is the ascending list of the mask row's set tokens,
+    4 keep + tail long, padded with -1 to budget + 3 entries."""
+    n = (p + 1) // 4
+    keep = min(budget // 4, n)
+    assert idx_row.shape == (budget + 3,)
+    assert count == 4 * keep + (p + 1) % 4, "count"
+    assert np.all(idx_row[count:] == -1), "padding"
+    got = idx_row[:count]
+    assert np.all(np.diff(got) > 0), "not ascending"
+    assert np.array_equal(got, np.flatnonzero(mask_row)), "tokens differ from the mask"
+
+
+@pytest.mark.parametrize("kind", ["zeros", "ties", "lowbyte", "wild", "equal", "random", "poison"])
+def test_select_indices_are_the_mask_tokens_in_order(kind):
+    scores, cols, pos, T = synth.selector_fixture(kind)
+    for budget in (2048, 64, 4):
+        mask, mst = O.select_mask(scores, cols, pos, T, budget)
+        idx, counts, ist = O.select_indices(scores, cols, pos, T, budget)
+        assert ist == mst
+        for r, p in enumerate(pos):
+            if mask[r].sum() == 0 and counts[r] == 0:
+                assert np.all(idx[r] == -1)  # refused row
+                continue
+            check_index_list(idx[r], int(counts[r]), mask[r], int(p), budget)
+
+
+def test_select_indices_brute_force_small_rows():
+    """Index lists of small rows from the O(n^2) rank definition: kept blocks
+    ascending, each as its 4 tokens, then the tail."""
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        n = int(rng.integers(0, 40))
+        p = 4 * n + int(rng.integers(0, 4)) - (1 if n and trial % 5 == 0 else 0)
+        p = max(p, 0)
+        n = (p + 1) // 4
+        budget = 4 * int(rng.integers(1, 20))
+        s = (rng.integers(-3, 4, size=max(n, 1)) * 0.5).astype(np.float32)
+        idx, count, st = O.select_indices_row(s, p, p + 1, budget)
+        assert st == 0
+        want = []
+        for b in rank_definition(s[:n], min(budget // 4, n)):
+            want.extend(range(4 * b, 4 * b + 4))
+        want.extend(range(4 * n, p + 1))
+        assert count == len(want) and np.array_equal(idx[:count], want)
+        assert np.all(idx[count:] == -1)
+
+
+def test_select_indices_under_budget_rows_are_the_prefix():
+    for p in (0, 1, 2, 3, 4, 67, 2047, 2050):
+        s = np.random.default_rng(p).standard_normal((p + 1) // 4 or 1).astype(np.float32)
+        idx, count, st = O.select_indices_row(s, p, 4096, 2048)
+        assert st == 0 and count == p + 1
+        assert np.array_equal(idx[:count], np.arange(p + 1)) and np.all(idx[count:] == -1)
+
+
+def test_select_indices_refusals_and_format_faults():
+    idx, count, st = O.select_indices_row(np.array([1.0, np.nan], np.float32), 7, 8, 64)
+    assert st == O.STATUS_NONFINITE_SCORE and count == 0 and np.all(idx == -1)
+    idx, count, st = O.select_indices_row(np.zeros(4, np.float32), 16, 16, 64)
+    assert st == O.STATUS_BAD_POSITION and count == 0 and np.all(idx == -1)
+    # planted faults in a copy of a good list are caught by the checks
+    scores, cols, pos, T = synth.selector_fixture("random", positions=(2054,))
+    mask, _ = O.select_mask(scores, cols, pos, T, 2048)
+    idx, counts, _ = O.select_indices(scores, cols, pos, T, 2048)
+    c = int(counts[0])
+    bad = {"no tail": (idx[0].copy(), c - 3), "unsorted": (idx[0].copy(), c),
+           "block start": (idx[0].copy(), c)}
+    bad["no tail"][0][c - 3:] = -1
+    bad["unsorted"][0][[0, 5]] = bad["unsorted"][0][[5, 0]]
+    bad["block start"][0][:c - 3] += 1
+    for name, (row, cnt) in bad.items():
+        with pytest.raises(AssertionError):
+            check_index_list(row, cnt, mask[0], 2054, 2048)
