@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -178,6 +178,34 @@ int qsa_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
 int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
                     const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
                     uint8_t* mask, int32_t* dev_status, void* stream);
+
+/*
+ * qsa_select_indices -- the same selection as qsa_select_mask, written as
+ * the list of visible token indices a sparse-attention gather consumes.
+ *
+ * [QSA] decode select (the host top-k it performs): the kept blocks sorted
+ * ascending, each expanded to its 4 tokens 4b .. 4b + 3, then the tail tokens
+ * 4n .. p; at most budget + 3 entries ([SCORE] "Next: P3": buffer bound
+ * budget + ratio - 1).  Kept set and order as in [SEL] "Exact semantics".
+ *
+ *   scores, score_cols, scores_len, pos, rows, tokens, budget, dev_status:
+ *               as for qsa_select_mask.
+ *   idx         [rows, idx_stride] int32, idx_stride >= budget + 3.  Row r's
+ *               entries [0, counts[r]) hold the ascending token indices,
+ *               entries [counts[r], budget + 3) hold -1; columns at or past
+ *               budget + 3 are untouched.  counts[r] = 4 min(budget/4, n) +
+ *               (p + 1) % 4, which is p + 1 for a row under the budget.
+ *   counts      [rows] int32.
+ *   A refused row (position out of range, non-finite score) gets count 0 and
+ *   -1 entries, and sets its QSA_STATUS_* bit.
+ * Refusals: those of qsa_select_mask, and QSA_ERR_STRIDE (idx_stride <
+ * budget + 3), QSA_ERR_EXTENT (idx_stride < 0), QSA_ERR_CAPACITY
+ * (rows * idx_stride overflows), QSA_ERR_NULL (idx or counts NULL).
+ */
+int qsa_select_indices(const float* scores, int64_t score_cols, int64_t scores_len,
+                       const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                       int32_t* idx, int64_t idx_stride, int32_t* counts, int32_t* dev_status,
+                       void* stream);
 
 /*
  * qsa_select_workspace_bytes -- device workspace qsa_select_mask_ws needs for

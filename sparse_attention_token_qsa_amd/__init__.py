@@ -18,7 +18,8 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
                    strerror)
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
-           "qsa_select_mask", "qsa_select_workspace_bytes", "qsa_select_mask_ws",
+           "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
+           "qsa_select_mask_ws",
            "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
@@ -171,6 +172,29 @@ def qsa_select_mask(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, to
     _check(lib.qsa_select_mask(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
                                budget, _ptr(mask), _ptr(dev_status), _stream_ptr(stream)),
            "qsa_select_mask")
+
+
+def qsa_select_indices(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, tokens: int,
+                       budget: int, idx: torch.Tensor, counts: torch.Tensor,
+                       dev_status: torch.Tensor, stream=None) -> None:
+    """Kept token indices of each row: idx [rows, >= budget + 3] int32
+    (ascending, -1 after counts[r]) and counts [rows] int32."""
+    _dev(scores, "scores", (torch.float32,))
+    _dev(pos, "pos", (torch.int32,))
+    _dev(idx, "idx", (torch.int32,))
+    _dev(counts, "counts", (torch.int32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous(), "pos must be contiguous")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    idx_stride = _rows_2d(idx, "idx", budget + RATIO - 1)
+    _need(idx.shape[0] >= rows, "idx needs a row per position")
+    _need(counts.is_contiguous() and counts.numel() >= rows, "counts must be contiguous [rows]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    lib = load()
+    _check(lib.qsa_select_indices(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
+                                  budget, _ptr(idx), idx_stride, _ptr(counts), _ptr(dev_status),
+                                  _stream_ptr(stream)), "qsa_select_indices")
 
 
 def qsa_select_workspace_bytes(rows: int, tokens: int) -> int:

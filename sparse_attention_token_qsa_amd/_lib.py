@@ -31,9 +31,9 @@ MAX_TOKENS = 262147
 
 # Every symbol the header declares.
 EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
-           "qsa_select_mask", "qsa_select_workspace_bytes", "qsa_select_mask_ws",
-           "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
-ABI_VERSION = 3
+           "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
+           "qsa_select_mask_ws", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
+ABI_VERSION = 4
 
 _lib = None
 
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_score_prepped.restype = ctypes.c_int
     lib.qsa_select_mask.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P]
     lib.qsa_select_mask.restype = ctypes.c_int
+    lib.qsa_select_indices.argtypes = [P, I64, I64, P, I64, I64, I64, P, I64, P, P, P]
+    lib.qsa_select_indices.restype = ctypes.c_int
     lib.qsa_select_workspace_bytes.argtypes = [I64, I64]
     lib.qsa_select_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_select_mask_ws.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P, I64, P]

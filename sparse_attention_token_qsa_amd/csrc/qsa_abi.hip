@@ -176,6 +176,28 @@ int qsa_select_mask(const float* scores, int64_t score_cols, int64_t scores_len,
                                           dev_status, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_select_indices(const float* scores, int64_t score_cols, int64_t scores_len,
+                       const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                       int32_t* idx, int64_t idx_stride, int32_t* counts, int32_t* dev_status,
+                       void* stream) {
+  if (rows < 0 || tokens < 0 || score_cols < 0 || scores_len < 0 || idx_stride < 0) return QSA_ERR_EXTENT;
+  if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
+    return QSA_ERR_BUDGET;
+  if (score_cols < tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  if (idx_stride < budget + QSA_RATIO - 1) return QSA_ERR_STRIDE;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
+  if (mul_overflows(rows, idx_stride, &need)) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0 || tokens == 0) return QSA_OK;
+  if (pos == nullptr || idx == nullptr || counts == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
+  if (tokens >= QSA_RATIO && scores == nullptr) return QSA_ERR_NULL;
+  return launch_status(qsa::launch_select_indices(scores, score_cols, pos, rows, tokens,
+                                                  static_cast<int>(budget / QSA_RATIO), idx, idx_stride,
+                                                  counts, dev_status, static_cast<hipStream_t>(stream)));
+}
+
 int64_t qsa_select_workspace_bytes(int64_t rows, int64_t tokens) {
   if (rows < 0 || tokens < 0) return QSA_ERR_EXTENT;
   if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;

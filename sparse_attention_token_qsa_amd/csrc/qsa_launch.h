@@ -34,6 +34,12 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
                          int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                          int32_t* status, hipStream_t stream);
 
+// Index-list output of the one-workgroup-per-row selector (select.hip).
+hipError_t launch_select_indices(const float* scores, int64_t score_cols, const int32_t* pos,
+                                 int64_t rows, int64_t tokens, int keep_max, int32_t* idx,
+                                 int64_t idx_stride, int32_t* counts, int32_t* status,
+                                 hipStream_t stream);
+
 // Split select for few long rows (select_split.hip): two launches over a
 // caller-provided workspace of select_split_workspace_bytes(rows, tokens).
 bool select_split_pays(int64_t rows, int64_t tokens);

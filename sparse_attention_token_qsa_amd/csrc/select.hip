@@ -48,17 +48,26 @@ struct SelectArgs {
   int keep_max;
   uint8_t* mask;
   int32_t* status;
+  int32_t* idx;        // index mode: [rows, idx_stride] kept token indices
+  int64_t idx_stride;
+  int32_t* counts;     // index mode: [rows] entries written
 };
 
-template <int NT, int KPT, int TOPM, bool VEC>
+// IDX: instead of the mask, row r's kept token indices in ascending order
+// (each kept block b as 4b .. 4b + 3, then the tail 4n .. p) go to
+// idx[r * idx_stride + i], i < counts[r] = 4 keep + tail, and -1 fills the
+// rest of the row's 4 keep_max + 3 entries; a refused row gets count 0.
+template <int NT, int KPT, int TOPM, bool VEC, bool IDX>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   constexpr int NW = NT / 64;
+  constexpr int kWords = IDX ? (KPT * NT + 31) / 32 : 1;  // bitmap of the row's blocks
   // The prefilter's per-wave rank r = ceil(512 / (NW * TOPM)) must stay <= 32.
   constexpr bool kPrefilter = NW * TOPM >= 16;
   constexpr int kCandCap = NT >= 1024 ? 4096 : 2048;
   __shared__ __attribute__((aligned(16))) uint32_t hist[3 * 256];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint64_t cand[kPrefilter ? kCandCap : 1];
+  __shared__ uint32_t kbits[kWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,8 +77,18 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   uint8_t* mrow = a.mask + row * T;
   const int64_t p = a.pos[row];
 
+  const int cap = 4 * a.keep_max + 3;  // index mode: entries per row
+  int32_t* irow = IDX ? a.idx + row * a.idx_stride : nullptr;
+  // index mode, rows without a selection: entries i <= last are i, the rest -1
+  auto write_prefix_idx = [&](int64_t last) {
+    for (int i = tid; i < cap; i += NT) irow[i] = i <= last ? i : -1;
+    if (tid == 0) a.counts[row] = static_cast<int32_t>(last + 1);
+  };
   if (p < 0 || p >= T) {
-    write_prefix_row<NT, VEC>(mrow, T, -1);
+    if constexpr (IDX)
+      write_prefix_idx(-1);
+    else
+      write_prefix_row<NT, VEC>(mrow, T, -1);
     if (tid == 0) atomicOr(a.status, 1);
     return;
   }
@@ -124,13 +143,21 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
     for (int j = 0; j < KPT; ++j) key[j] = 0u;
   }
   if (tid < 256) hist[tid] = 0u;  // first radix buffer; the next barrier publishes it
+  if constexpr (IDX)
+    for (int i = tid; i < kWords; i += NT) kbits[i] = 0u;
   if (__syncthreads_or(bad)) {
-    write_prefix_row<NT, VEC>(mrow, T, -1);
+    if constexpr (IDX)
+      write_prefix_idx(-1);
+    else
+      write_prefix_row<NT, VEC>(mrow, T, -1);
     if (tid == 0) atomicOr(a.status, 2);
     return;
   }
   if (n <= keep) {  // every block kept: the visible prefix [0, p]
-    write_prefix_row<NT, VEC>(mrow, T, p);
+    if constexpr (IDX)
+      write_prefix_idx(p);
+    else
+      write_prefix_row<NT, VEC>(mrow, T, p);
     return;
   }
 
@@ -246,6 +273,53 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   auto kept = [&](uint32_t kk, int b) {
     return kk >= lowkey && (kk > khi || (kk == khi && static_cast<int64_t>(b) <= blim));
   };
+  if constexpr (IDX) {
+    // kept blocks into the bitmap, then each thread takes a run of words:
+    // an exclusive scan of the runs' popcounts is the rank of the run's
+    // first kept block, and its blocks follow in ascending order.
+    const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
+      if (b < n && kept(opaque(key[j]), b)) atomicOr(&kbits[b >> 5], 1u << (b & 31));
+    }
+    __syncthreads();
+    const int words = (n + 31) >> 5;
+    constexpr int WPT = (kWords + NT - 1) / NT;
+    uint32_t wv[WPT];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int w = tid * WPT + i;
+      wv[i] = w < words ? kbits[w] : 0u;
+      mine += static_cast<uint32_t>(__popc(wv[i]));
+    }
+    const uint32_t incl = wave_incl_sum(mine);
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    uint32_t rank = incl - mine;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rank += w < wave ? red[w] : 0u;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      uint32_t bits = wv[i];
+      while (bits) {
+        const int b = 32 * (tid * WPT + i) + __ffs(bits) - 1;
+        bits &= bits - 1u;
+        int32_t* dst = irow + 4 * rank;
+        dst[0] = 4 * b;
+        dst[1] = 4 * b + 1;
+        dst[2] = 4 * b + 2;
+        dst[3] = 4 * b + 3;
+        ++rank;
+      }
+    }
+    // tail tokens 4n .. p after the 4 keep block tokens, then -1
+    const int tail = static_cast<int>(p + 1) - 4 * n;
+    for (int i = 4 * keep + tid; i < cap; i += NT) irow[i] = i < 4 * keep + tail ? 4 * n + (i - 4 * keep) : -1;
+    if (tid == 0) a.counts[row] = 4 * keep + tail;
+    return;
+  }
   if constexpr (VEC) {
 #pragma unroll
     for (int g = 0; g < KPT / 4; ++g) {
@@ -277,13 +351,27 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   }
 }
 
-template <int NT, int KPT, int TOPM>
+template <int NT, int KPT, int TOPM, bool IDX>
 hipError_t launch_select_t(const SelectArgs& a, int64_t rows, bool vec, hipStream_t stream) {
   if (vec)
-    select_kernel<NT, KPT, TOPM, true><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+    select_kernel<NT, KPT, TOPM, true, IDX><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
   else
-    select_kernel<NT, KPT, TOPM, false><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+    select_kernel<NT, KPT, TOPM, false, IDX><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool IDX>
+hipError_t launch_select_rows(const SelectArgs& a, int64_t rows, bool vec, hipStream_t stream) {
+  const int64_t nmax = a.tokens / kRatio;
+  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (nmax <= 1024) return launch_select_t<256, 4, 1, IDX>(a, rows, vec, stream);
+  if (nmax <= 2048) return launch_select_t<256, 8, 1, IDX>(a, rows, vec, stream);
+  if (nmax <= 4096) return launch_select_t<256, 16, 1, IDX>(a, rows, vec, stream);
+  if (nmax <= 8192) return launch_select_t<512, 16, 2, IDX>(a, rows, vec, stream);
+  if (nmax <= 16384) return launch_select_t<512, 32, 2, IDX>(a, rows, vec, stream);
+  if (nmax <= 32768) return launch_select_t<1024, 32, 1, IDX>(a, rows, vec, stream);
+  if (nmax <= 65536) return launch_select_t<1024, 64, 1, IDX>(a, rows, vec, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -302,16 +390,26 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
   // 16-byte loads of 4 scores and 16-byte mask stores of 4 blocks
   const bool vec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0) &&
                    (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
-  const int64_t nmax = tokens / kRatio;
-  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (nmax <= 1024) return launch_select_t<256, 4, 1>(a, rows, vec, stream);
-  if (nmax <= 2048) return launch_select_t<256, 8, 1>(a, rows, vec, stream);
-  if (nmax <= 4096) return launch_select_t<256, 16, 1>(a, rows, vec, stream);
-  if (nmax <= 8192) return launch_select_t<512, 16, 2>(a, rows, vec, stream);
-  if (nmax <= 16384) return launch_select_t<512, 32, 2>(a, rows, vec, stream);
-  if (nmax <= 32768) return launch_select_t<1024, 32, 1>(a, rows, vec, stream);
-  if (nmax <= 65536) return launch_select_t<1024, 64, 1>(a, rows, vec, stream);
-  return hipErrorInvalidValue;
+  return launch_select_rows<false>(a, rows, vec, stream);
+}
+
+hipError_t launch_select_indices(const float* scores, int64_t score_cols, const int32_t* pos,
+                                 int64_t rows, int64_t tokens, int keep_max, int32_t* idx,
+                                 int64_t idx_stride, int32_t* counts, int32_t* status,
+                                 hipStream_t stream) {
+  SelectArgs a{};
+  a.scores = scores;
+  a.score_cols = score_cols;
+  a.pos = pos;
+  a.tokens = tokens;
+  a.keep_max = keep_max;
+  a.status = status;
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.counts = counts;
+  // 16-byte loads of 4 scores
+  const bool vec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+  return launch_select_rows<true>(a, rows, vec, stream);
 }
 
 }  // namespace qsa

@@ -121,3 +121,16 @@ def gpu_select_ws(scores: np.ndarray, cols: int, pos, tokens: int, budget: int, 
     qsa.qsa_select_mask_ws(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, mask, st, ws)
     s = qsa.check_status(st)
     return mask.cpu().numpy(), s, nbytes
+
+
+def gpu_select_indices(scores: np.ndarray, cols: int, pos, tokens: int, budget: int, stride=None):
+    """qsa_select_indices: (idx [rows, stride] read back, counts, status);
+    idx is prefilled with a sentinel so untouched columns show."""
+    rows = len(pos)
+    stride = budget + 3 if stride is None else stride
+    idx = torch.full((rows, stride), -77, dtype=torch.int32, device=DEV)
+    counts = torch.full((rows,), -77, dtype=torch.int32, device=DEV)
+    st = status_word()
+    qsa.qsa_select_indices(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, idx, counts, st)
+    s = qsa.check_status(st)
+    return idx.cpu().numpy(), counts.cpu().numpy(), s

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 3
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 4
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -148,6 +148,32 @@ def test_select_refusals(lib):
     assert select(lib, scores_len=127) == CAP
     assert select(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
     assert select(lib, rows=2**40, score_cols=16, scores_len=2**62) == CAP
+
+
+def select_idx(lib, **kw):
+    a = dict(scores=P, score_cols=16, scores_len=128, pos=P, rows=8, tokens=64, budget=2048,
+             idx=P, idx_stride=2051, counts=P, status=P)
+    a.update(kw)
+    return lib.qsa_select_indices(a["scores"], a["score_cols"], a["scores_len"], a["pos"], a["rows"],
+                                  a["tokens"], a["budget"], a["idx"], a["idx_stride"], a["counts"],
+                                  a["status"], None)
+
+
+def test_select_indices_refusals(lib):
+    assert select_idx(lib, rows=0) == OK
+    assert select_idx(lib, tokens=0, score_cols=0) == OK
+    for k in ("scores", "pos", "idx", "counts", "status"):
+        assert select_idx(lib, **{k: None}) == NULL, k
+    assert select_idx(lib, rows=-1) == EXTENT
+    assert select_idx(lib, idx_stride=-1) == EXTENT
+    for b in (0, -4, 2, 2052):
+        assert select_idx(lib, budget=b) == BUDGET, b
+    assert select_idx(lib, score_cols=15) == STRIDE
+    assert select_idx(lib, idx_stride=2050) == STRIDE
+    assert select_idx(lib, budget=64, idx_stride=66) == STRIDE
+    assert select_idx(lib, budget=64, idx_stride=67, rows=0) == OK
+    assert select_idx(lib, scores_len=127) == CAP
+    assert select_idx(lib, rows=2**40, score_cols=16, scores_len=2**62, idx_stride=2**30) == CAP
 
 
 def select_ws(lib, **kw):

@@ -15,7 +15,7 @@ import torch
 import oracle as O
 import synth
 from tests.gpu_util import (DEV, gpu_pool, gpu_prep, gpu_scores, gpu_scores_prepped, gpu_select,
-                            gpu_select_ws, note, u16_dev, u16_host, workload)
+                            gpu_select_indices, gpu_select_ws, note, u16_dev, u16_host, workload)
 from tests.test_oracle_pins import check_structure
 
 pytestmark = pytest.mark.gpu
@@ -208,6 +208,60 @@ def test_select_longest_supported_row():
         want, _ = O.select_mask(scores, cols, pos2, T, 2048)
         got, st = gpu_select(scores, cols, pos2, T, 2048)
         assert st == 0 and np.array_equal(got, want)
+
+
+# ------------------------------------------------- select, index lists ----
+
+def _check_indices(got, gcnt, want, wcnt, budget, stride):
+    bad = [r for r in range(len(wcnt))
+           if gcnt[r] != wcnt[r] or not np.array_equal(got[r, : budget + 3], want[r])]
+    assert not bad, bad[:5]
+    assert np.all(got[:, budget + 3: stride] == -77), "wrote past budget + 3"
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_select_indices_on_oracle_scores_bit_exact(wid):
+    w = workload(wid)
+    rows = sample_rows(wid)
+    if wid == 5:
+        rows = rows[:48]
+    T = w["tokens"]
+    cols = T // 4
+    sc = dense(oracle_scores(wid, rows), cols)
+    pos = w["pos"][rows]
+    b = w["budget"]
+    note(f"index lists on oracle scores: workload {wid}, {len(rows)} rows")
+    want, wcnt, wst = O.select_indices(sc, cols, pos, T, b)
+    got, gcnt, gst = gpu_select_indices(sc, cols, pos, T, b, stride=b + 9)
+    assert gst == wst == 0
+    _check_indices(got, gcnt, want, wcnt, b, b + 9)
+
+
+@pytest.mark.parametrize("kind", ["zeros", "ties", "lowbyte", "wild", "equal", "random", "poison"])
+def test_select_indices_fixtures_bit_exact(kind):
+    scores, cols, pos, T = synth.selector_fixture(kind)
+    note(f"index lists, fixture {kind}: rows {len(pos)}, tokens {T}")
+    for budget in (2048, 64, 4):
+        want, wcnt, wst = O.select_indices(scores, cols, pos, T, budget)
+        got, gcnt, gst = gpu_select_indices(scores, cols, pos, T, budget)
+        assert gst == wst
+        _check_indices(got, gcnt, want, wcnt, budget, budget + 3)
+
+
+def test_select_indices_ragged_tokens_spare_columns_bad_positions():
+    for T in (4099, 16387, 65541, 5, 1):
+        pos = np.array([T - 1, 0, T // 2, -1, T, 2 * T + 5, max(T - 3, 0)], dtype=np.int32)
+        cols = T // 4 + 11
+        scores = np.full((len(pos), cols), np.nan, np.float32)
+        rng = np.random.default_rng(T)
+        for r, p in enumerate(pos):
+            n = (int(p) + 1) // 4 if 0 <= p < T else 0
+            scores[r, :n] = rng.standard_normal(n)
+        note(f"index lists ragged: tokens {T}")
+        want, wcnt, wst = O.select_indices(scores, cols, pos, T, 64)
+        got, gcnt, gst = gpu_select_indices(scores, cols, pos, T, 64, stride=70)
+        assert gst == wst
+        _check_indices(got, gcnt, want, wcnt, 64, 70)
 
 
 # ------------------------------------------------- select, split rows ----
