@@ -463,14 +463,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
 
 
 // ---------------------------------------------------------------------------
-// Ring scorer for prepared queries and long row batches (prefill).
+// Ring scorer for prepared queries.
 //
-// 128 query rows per workgroup: wave w holds rows 32 w .. 32 w + 31 as four
-// 32 x 128 A-fragment sets (MS = 4) for the whole block loop.  Each step
-// takes one 32-block tile: the pooled keys stream through a D-stage LDS ring
+// WM waves along M, each holding 32 query rows as four 32 x 128 A-fragment
+// sets (MS = 4) for the whole block loop: 32 WM rows per workgroup.  The
+// other 4 / WM wave columns split each step's tile of 32 (4 / WM) blocks,
+// 32 blocks per wave.  Prefill batches take WM = 4 (128 rows, 32-block
+// tiles).  The pooled keys stream through a D-stage LDS ring
 // filled by buffer loads straight to LDS (blocks at or past the workgroup's
-// longest prefix read as zeros and are never stored), and every wave reads
-// the tile's eight B fragments once and feeds each to four MFMAs.
+// longest prefix read as zeros and are never stored); every wave reads its
+// eight B fragments of a step once and feeds each to four MFMAs.
 //
 // Two details keep the ring pipelined.  The B-fragment reads are inline
 // assembly: a compiler-visible LDS read behind an in-flight load to LDS makes
@@ -484,9 +486,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
 // so relu / head sum / scale of one pair overlaps the other pair's MFMAs.
 // ---------------------------------------------------------------------------
 
-constexpr int kRingRows = 128;  // query rows per workgroup
-constexpr int kRingTile = 32;   // blocks per step
-constexpr int kRingStages = 4;
+template <int WM>
+struct RingGeom {
+  static constexpr int WN = 4 / WM;
+  static constexpr int RG = 32 * WM;          // query rows per workgroup
+  static constexpr int TILE = 32 * WN;        // blocks per step
+  static constexpr int STAGE = TILE * 256;    // bytes per ring stage
+  static constexpr int kL = STAGE / 4096;     // 1 KiB ring loads per wave per tile
+  static constexpr int kStores = 16;          // score stores per wave per step
+  static constexpr int D = WM == 4 ? 4 : 3;   // ring stages
+};
 
 struct RingArgs {
   const uint16_t* qhat;
@@ -539,16 +548,17 @@ __device__ __forceinline__ float pair_score(const f32x16_t& acc, int q4) {
   return s * (0.5f * kScale);
 }
 
-template <int D>
+template <int WM>
 __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
-  constexpr int RG = kRingRows, TILE = kRingTile, STAGE = TILE * 256;
-  constexpr int kL = 2;        // 1 KiB ring loads per wave per tile
-  constexpr int kStores = 16;  // score stores per wave per step
+  using G = RingGeom<WM>;
+  constexpr int RG = G::RG, TILE = G::TILE, STAGE = G::STAGE, kL = G::kL, kStores = G::kStores, D = G::D;
   __shared__ __attribute__((aligned(16))) unsigned char ring[D * STAGE];
   __shared__ int nvis[RG];
   __shared__ int sh_nmax, sh_nmin;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = wave % WM;   // 32-row slice of the group
+  const int ng = wave / WM;  // 32-block slice of the tile
   // consecutive tasks (the splits of one row group) share an XCD, so their
   // neighbouring pieces of the same score rows meet in one L2
   int task = blockIdx.x;
@@ -562,13 +572,13 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   const int blk_begin = split * TILE;
   const int stride = a.splits * TILE;
 
-  // A fragments: subtile ms of wave w = rows 32 w + 8 ms .. + 7 as 32 M-rows (row, head)
+  // A fragments: subtile ms = rows 32 m + 8 ms .. + 7 as 32 M-rows (row, head)
   bf16x8_t afrag[4][8];
   {
     const int khalf = 8 * (lane >> 5);
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
-      int64_t rr = row0 + 32 * wave + 8 * ms + ((lane & 31) >> 2);
+      int64_t rr = row0 + 32 * m + 8 * ms + ((lane & 31) >> 2);
       rr = rr < a.rows ? rr : a.rows - 1;  // rows past the end are never stored
       const uint16_t* src = a.qhat + rr * (kHeads * kHeadDim) + kHeadDim * (lane & 3) + khalf;
 #pragma unroll
@@ -579,20 +589,22 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   if (wave == 0) {
     uint32_t mx = 0u, mn = 0x7FFFFFFFu;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < (RG + 63) / 64; ++hh) {
       const int lr = lane + 64 * hh;
-      int n = 0;
-      const int64_t r = row0 + lr;
-      if (r < a.rows) {
-        const int p = a.pos[r];
-        if (p >= 0 && p < a.tokens)
-          n = (p + 1) / kRatio;
-        else if (split == 0)
-          atomicOr(a.status, 1);
+      if (lr < RG) {
+        int n = 0;
+        const int64_t r = row0 + lr;
+        if (r < a.rows) {
+          const int p = a.pos[r];
+          if (p >= 0 && p < a.tokens)
+            n = (p + 1) / kRatio;
+          else if (split == 0)
+            atomicOr(a.status, 1);
+        }
+        nvis[lr] = n;
+        mx = max(mx, static_cast<uint32_t>(n));
+        mn = min(mn, static_cast<uint32_t>(n));
       }
-      nvis[lr] = n;
-      mx = max(mx, static_cast<uint32_t>(n));
-      mn = min(mn, static_cast<uint32_t>(n));
     }
     mx = wave_max_u32(mx);
     mn = wave_min_u32(mn);
@@ -606,7 +618,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   const int nmin = sh_nmin;  // blocks every row of the workgroup sees
   if (blk_begin >= nmax) return;  // uniform; nothing in flight
 
-  // ---- key ring.  Load i of wave w fills tile rows 4 (2 w + i) + lane / 16
+  // ---- key ring.  Load i of wave w fills tile rows 4 (w kL + i) + lane / 16
   // with the key's 16-byte chunk (lane % 16) ^ (row & 7) at chunk lane % 16,
   // so a B-fragment read (32 rows, one chunk each) spreads over all banks.
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -624,20 +636,21 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
 #pragma unroll
   for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t);
 
-  // B fragment ks of lane (r, h): stage row r, logical chunk 2 ks + h at
-  // chunk (2 ks + h) ^ (r & 7) = 2 ((ks & 3) ^ s2) + (h ^ s1) + 8 (ks >> 2).
+  // B fragment ks of lane (r, h): stage row 32 ng + r, logical chunk 2 ks + h
+  // at chunk (2 ks + h) ^ (r & 7) = 2 ((ks & 3) ^ s2) + (h ^ s1) + 8 (ks >> 2).
   const int r = lane & 31, h = lane >> 5;
+  const int col = 32 * ng + r;  // the lane's block within the tile
   const int s2 = (r & 7) >> 1, s1 = r & 1;
-  const uint32_t bbase = lds_addr(ring) + r * 256 + 16 * (h ^ s1);
+  const uint32_t bbase = lds_addr(ring) + col * 256 + 16 * (h ^ s1);
   const uint32_t s2x = 32 * s2;
-  const uint32_t nvis_lane = lds_addr(nvis) + 4 * (32 * wave + h);
+  const uint32_t nvis_lane = lds_addr(nvis) + 4 * (32 * m + h);
 
   // score stores through a resource over the group's rows: lane (r, h) of
-  // subtile ms writes row 32 w + 8 ms + 2 q4 + h, column nb0 + r.  An offset
-  // past the resource drops the store (blocks outside a row's prefix).
+  // subtile ms writes row 32 m + 8 ms + 2 q4 + h, column nb0 + col.  An
+  // offset past the resource drops the store (blocks outside a row's prefix).
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.scores + row0 * a.score_cols, static_cast<short>(0), static_cast<int>(RG * a.score_cols * 4), 0x00020000);
-  const int vbase = ((32 * wave + h) * static_cast<int>(a.score_cols) + r) * 4;
+  const int vbase = ((32 * m + h) * static_cast<int>(a.score_cols) + col) * 4;
   const int rowbytes = static_cast<int>(a.score_cols) * 4;
   constexpr int kDrop = static_cast<int>(0x80000000u);
 
@@ -654,7 +667,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       int off = vbase;
       if (!fast) {
         const int nv = lds_read_word(nvis_lane + 4 * (8 * ms + 2 * q4));
-        off = (live && nb0 + r < nv) ? vbase : kDrop;
+        off = (live && nb0 + col < nv) ? vbase : kDrop;
       }
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[j]), orsrc, off,
                                             (8 * ms + 2 * q4) * rowbytes + 4 * nb0, 0);
@@ -708,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
     // Tile t + 1 has landed once at most N of this wave's memory operations
     // are outstanding, N = what was issued after its loads: the loads of
     // (D - 2) tiles and the 16 stores of each step since (D - 1 steps in the
-    // steady state, step + 1 in the first D - 2 steps).
+    // steady state, step + 1 in the first D - 2 steps).  Smaller N is safe.
     {
       constexpr int NA0 = (D - 2) * kL + (D - 1) * kStores;
       constexpr int NA = NA0 > 63 ? 63 : NA0;
@@ -731,7 +744,11 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
-hipError_t launch_score_ring(const ScoreArgs& base, hipStream_t stream) {
+// Workgroups: `target` in all, at least one tile each; a row group's splits
+// take interleaved tiles.
+template <int WM>
+hipError_t launch_score_ring_geom(const ScoreArgs& base, int64_t target, hipStream_t stream) {
+  using G = RingGeom<WM>;
   RingArgs a{};
   a.qhat = base.qhat;
   a.pos = base.pos;
@@ -742,17 +759,26 @@ hipError_t launch_score_ring(const ScoreArgs& base, hipStream_t stream) {
   a.score_cols = base.score_cols;
   a.status = base.status;
   const int64_t nb_total = a.tokens / kRatio;
-  const int64_t row_groups = (a.rows + kRingRows - 1) / kRingRows;
-  int64_t n_tiles = (nb_total + kRingTile - 1) / kRingTile;
+  const int64_t row_groups = (a.rows + G::RG - 1) / G::RG;
+  int64_t n_tiles = (nb_total + G::TILE - 1) / G::TILE;
   if (n_tiles < 1) n_tiles = 1;
-  int64_t splits = (1024 + row_groups - 1) / row_groups;
+  int64_t splits = (target + row_groups - 1) / row_groups;
   if (splits < 1) splits = 1;
   if (splits > n_tiles) splits = n_tiles;
   if (row_groups * splits > 0x7FFFFFFF) return hipErrorInvalidValue;
   a.splits = static_cast<int>(splits);
   a.tasks = static_cast<int>(row_groups * splits);
-  score_ring_kernel<kRingStages><<<dim3(static_cast<unsigned>(a.tasks)), dim3(256), 0, stream>>>(a);
+  score_ring_kernel<WM><<<dim3(static_cast<unsigned>(a.tasks)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+// The ring's store resource spans 32 WM rows of scores, within 2^31 bytes.
+bool ring_fits(const ScoreArgs& a, int rows_per_group) {
+  return a.score_cols <= 0x7FFFFFFF / (4 * rows_per_group);
+}
+
+hipError_t launch_score_ring(const ScoreArgs& a, hipStream_t stream) {
+  return launch_score_ring_geom<4>(a, 1024, stream);
 }
 
 template <int WM, int MS, int D, bool PREP>
@@ -786,10 +812,12 @@ hipError_t launch_score_rows(const ScoreArgs& a, hipStream_t stream) {
   // Prepared queries: 32 rows per wave when there are enough rows, so each
   // B fragment feeds four MFMAs.  The one-call path keeps 8 rows per wave,
   // which bounds its query-prep LDS.
-  // Prepared queries, long batches: the ring scorer (its store resource
-  // spans 128 rows of scores, within 2^31 bytes).
+  // Prepared queries in batches of 128 rows and more: the ring scorer, when
+  // its store resource fits.  (Its 1- and 2-wave-row layouts measured slower
+  // than the kernels below on decode batches: 32 A-fragment loads and a
+  // 96 KiB ring per workgroup outweigh the shared key tiles there.)
   if constexpr (PREP)
-    if (a.rows >= kRingRows && a.score_cols <= 0x7FFFFFFF / (4 * kRingRows)) return launch_score_ring(a, stream);
+    if (a.rows >= 128 && ring_fits(a, 128)) return launch_score_ring(a, stream);
   if constexpr (PREP)
     if (a.rows >= 64) return launch_score_geom<2, 4, 4, PREP>(a, stream);
   if (a.rows >= 32) return launch_score_geom<4, 1, 4, PREP>(a, stream);
