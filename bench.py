@@ -228,11 +228,12 @@ STAGE_SOURCES = {
     "pool": ["pool.hip", "qsa_device.h"],
     "prep": ["prep.hip", "qsa_device.h"],
     "score": ["score.hip", "qsa_device.h"],
-    "select": ["select.hip", "qsa_device.h"],
+    "select": ["select.hip", "select_split.hip", "select_common.h", "qsa_device.h"],
 }
-# kernel-name fragment of each stage in rocprofv3 output
-STAGE_KERNELS = {"pool": "pool_kernel", "prep": "prep_kernel", "score": "score_mfma_kernel",
-                 "select": "select_kernel"}
+# kernel-name fragment of each stage in rocprofv3 output (a stage may launch
+# several kernels: the split select launches a chunk and a merge kernel)
+STAGE_KERNELS = {"pool": "pool_kernel", "prep": "prep_kernel", "score": "score_",
+                 "select": "select_"}
 COPY_BYTES = 512 << 20  # the counter pass's calibration copy
 
 
@@ -317,17 +318,23 @@ def traffic_table(fetch_dir: str, write_dir: str, workload: int):
         cal = median([v for v in copies if v >= 0.5 * top])
         factor = COPY_BYTES / cal  # bytes per counter unit
         for st, frag in STAGE_KERNELS.items():
-            vals = [v for _, k, v in rows if frag in k]
-            if vals:
-                per.setdefault(st, {})[counter] = (median(vals), factor, len(vals))
+            names = sorted({k for _, k, _ in rows if frag in k})
+            if not names:
+                continue
+            # one launch of the stage: the median dispatch of each of its kernels
+            total = sum(median([v for _, k, v in rows if k == name]) for name in names)
+            n = min(sum(1 for _, k, _ in rows if k == name) for name in names)
+            short = [name.replace("void ", "").replace("qsa::(anonymous namespace)::", "").split("(")[0]
+                     for name in names]
+            per.setdefault(st, {})[counter] = (total, factor, n, short)
     for st, c in per.items():
         if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
             continue
-        fk, ff, n1 = c["FETCH_SIZE"]
-        wk, wf, n2 = c["WRITE_SIZE"]
+        fk, ff, n1, names = c["FETCH_SIZE"]
+        wk, wf, n2, _ = c["WRITE_SIZE"]
         rd, wr = fk * ff, wk * wf
         table[f"{st}:{name}"] = {
-            "kernel": STAGE_KERNELS[st], "fetch_kib": fk, "write_kib": wk,
+            "kernel": " + ".join(names), "fetch_kib": fk, "write_kib": wk,
             "fetch_bytes_per_unit": round(ff, 2), "write_bytes_per_unit": round(wf, 2),
             "dispatches": [n1, n2], "read_bytes": round(rd), "write_bytes": round(wr),
             "hbm_bytes_per_launch": round(rd + wr), "source_sha": source_hash(st)}
