@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -239,6 +239,50 @@ int qsa_select_mask_ws(const float* scores, int64_t score_cols, int64_t scores_l
                        const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
                        uint8_t* mask, int32_t* dev_status, void* workspace,
                        int64_t workspace_bytes, void* stream);
+
+/*
+ * qsa_score_select_workspace_bytes -- device workspace qsa_score_select_mask
+ * needs for `rows` rows over a `tokens`-token cache at `budget`: a full
+ * score matrix for the rows that fall back (rows * tokens bytes), sampled
+ * scores (rows * tokens / 16 bytes) and candidate regions (8192 rows of 65536
+ * tokens at budget 2048: 0.82 GB in all).  0 for an empty call;
+ * QSA_ERR_EXTENT / QSA_ERR_BUDGET / QSA_ERR_CAPACITY as for
+ * qsa_score_select_mask.
+ */
+int64_t qsa_score_select_workspace_bytes(int64_t rows, int64_t tokens, int64_t budget);
+
+/*
+ * qsa_score_select_mask -- qsa_score_prepped followed by qsa_select_mask, as
+ * one call that does not write the block scores out: the same mask bytes and
+ * status bits, bit for bit.
+ *
+ * [SCORE] "Next" names a fused score -> select pass for long prefill; [SEL]
+ * "Exact semantics" fixes the kept set.  Each row's keep-th largest block is
+ * found among the blocks scoring at or above a per-row threshold taken from
+ * every 16th block's score; a row whose threshold admits fewer than
+ * budget/4 blocks, or more than the workspace holds, is scored and selected
+ * again in full, inside the same call.  The result never depends on the
+ * threshold; the time does.  Meant for prefill batches (many rows sharing
+ * one cache); it works for any batch.
+ *
+ *   qhat        [rows, 4, 128] bf16 from qsa_prep_queries.
+ *   pos, rows, pooled, tokens, budget, mask, dev_status: as for
+ *               qsa_score_prepped and qsa_select_mask.
+ *   workspace   device memory owned by the caller, 256-byte aligned, at least
+ *               workspace_bytes >= qsa_score_select_workspace_bytes(rows,
+ *               tokens, budget) long; contents on entry do not matter, on
+ *               return unspecified.  Two calls in flight on the same
+ *               workspace race.
+ * Refusals: QSA_ERR_EXTENT (negative rows, tokens or workspace_bytes),
+ * QSA_ERR_BUDGET, QSA_ERR_CAPACITY (tokens > QSA_MAX_TOKENS, rows >
+ * INT32_MAX, rows * tokens overflows, workspace_bytes too small),
+ * QSA_ERR_NULL (qhat, pos, mask, dev_status or workspace NULL; pooled NULL
+ * with tokens >= 4), QSA_ERR_PARAM (workspace not 256-byte aligned).
+ */
+int qsa_score_select_mask(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                          const uint16_t* pooled, int64_t tokens, int64_t budget, uint8_t* mask,
+                          int32_t* dev_status, void* workspace, int64_t workspace_bytes,
+                          void* stream);
 
 /*
  * qsa_rope_inv_freq -- host only: the rotary frequencies the kernels use,

@@ -19,7 +19,7 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
-           "qsa_select_mask_ws",
+           "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
            "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
@@ -228,6 +228,41 @@ def qsa_select_mask_ws(scores: torch.Tensor, score_cols: int, pos: torch.Tensor,
     _check(lib.qsa_select_mask_ws(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
                                   budget, _ptr(mask), _ptr(dev_status), _ptr(workspace), ws_bytes,
                                   _stream_ptr(stream)), "qsa_select_mask_ws")
+
+
+def qsa_score_select_workspace_bytes(rows: int, tokens: int, budget: int) -> int:
+    """Device workspace bytes qsa_score_select_mask needs."""
+    n = load().qsa_score_select_workspace_bytes(rows, tokens, budget)
+    if n < 0:
+        raise QsaError(int(n), "qsa_score_select_workspace_bytes")
+    return int(n)
+
+
+def qsa_score_select_mask(qhat: torch.Tensor, pos: torch.Tensor, pooled: torch.Tensor, tokens: int,
+                          budget: int, mask: torch.Tensor, dev_status: torch.Tensor,
+                          workspace: torch.Tensor, stream=None) -> None:
+    """qsa_score_prepped followed by qsa_select_mask in one call, without the
+    score matrix: `workspace` is a device tensor of at least
+    qsa_score_select_workspace_bytes(rows, tokens, budget) bytes, 256-byte
+    aligned (torch's allocations are)."""
+    _dev(qhat, "qhat", _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(pooled, "pooled", _BF16_LIKE)
+    _dev(mask, "mask", (torch.uint8,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous() and qhat.is_contiguous() and pooled.is_contiguous(),
+          "qhat, pos and pooled must be contiguous")
+    _need(qhat.numel() >= rows * HEADS * HEAD_DIM, "qhat must hold [rows, 4, 128]")
+    _need(pooled.numel() >= (tokens // RATIO) * HEAD_DIM, "pooled must hold [tokens/4, 128]")
+    _need(mask.is_contiguous() and mask.numel() >= rows * tokens, "mask must be contiguous [rows, tokens]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    _check(lib.qsa_score_select_mask(_ptr(qhat), _ptr(pos), rows, _ptr(pooled), tokens, budget, _ptr(mask),
+                                     _ptr(dev_status), _ptr(workspace), ws_bytes, _stream_ptr(stream)),
+           "qsa_score_select_mask")
 
 
 def qsa_rope_inv_freq(rotary_dim: int, rope_theta: float) -> list:

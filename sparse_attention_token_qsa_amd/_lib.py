@@ -32,8 +32,9 @@ MAX_TOKENS = 262147
 # Every symbol the header declares.
 EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
-           "qsa_select_mask_ws", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
-ABI_VERSION = 4
+           "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
+           "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
+ABI_VERSION = 5
 
 _lib = None
 
@@ -70,6 +71,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_select_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_select_mask_ws.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P, I64, P]
     lib.qsa_select_mask_ws.restype = ctypes.c_int
+    lib.qsa_score_select_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.qsa_score_select_workspace_bytes.restype = ctypes.c_int64
+    lib.qsa_score_select_mask.argtypes = [P, P, I64, P, I64, I64, P, P, P, I64, P]
+    lib.qsa_score_select_mask.restype = ctypes.c_int
     lib.qsa_rope_inv_freq.argtypes = [I32, F, P]
     lib.qsa_rope_inv_freq.restype = ctypes.c_int
     lib.qsa_strerror.argtypes = [ctypes.c_int]

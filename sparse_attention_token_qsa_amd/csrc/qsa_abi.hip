@@ -223,4 +223,37 @@ int qsa_select_mask_ws(const float* scores, int64_t score_cols, int64_t scores_l
                                                 dev_status, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int64_t qsa_score_select_workspace_bytes(int64_t rows, int64_t tokens, int64_t budget) {
+  if (rows < 0 || tokens < 0) return QSA_ERR_EXTENT;
+  if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
+    return QSA_ERR_BUDGET;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0 || tokens == 0) return 0;
+  return qsa::score_select_workspace_bytes(rows, tokens, static_cast<int>(budget / QSA_RATIO));
+}
+
+int qsa_score_select_mask(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                          const uint16_t* pooled, int64_t tokens, int64_t budget, uint8_t* mask,
+                          int32_t* dev_status, void* workspace, int64_t workspace_bytes,
+                          void* stream) {
+  if (rows < 0 || tokens < 0 || workspace_bytes < 0) return QSA_ERR_EXTENT;
+  if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
+    return QSA_ERR_BUDGET;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, tokens, &need)) return QSA_ERR_CAPACITY;
+  if (rows == 0 || tokens == 0) return QSA_OK;
+  if (qhat == nullptr || pos == nullptr || mask == nullptr || dev_status == nullptr ||
+      workspace == nullptr)
+    return QSA_ERR_NULL;
+  if (tokens >= QSA_RATIO && pooled == nullptr) return QSA_ERR_NULL;
+  const int keep_max = static_cast<int>(budget / QSA_RATIO);
+  if (workspace_bytes < qsa::score_select_workspace_bytes(rows, tokens, keep_max)) return QSA_ERR_CAPACITY;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return QSA_ERR_PARAM;
+  return launch_status(qsa::launch_score_select(qhat, pos, rows, pooled, tokens, keep_max, mask, dev_status,
+                                                workspace, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

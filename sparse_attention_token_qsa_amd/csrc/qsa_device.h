@@ -11,6 +11,8 @@ constexpr int kHeadDim = 128;
 constexpr int kRatio = 4;
 constexpr int kMaxKeep = 512;
 constexpr int kMaxHalfRotary = 64;
+// score scale 1/sqrt(head dim), rounded once to f32
+constexpr float kScale = static_cast<float>(0.088388347648318440550);
 
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

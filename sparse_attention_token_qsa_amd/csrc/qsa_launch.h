@@ -48,4 +48,47 @@ hipError_t launch_select_split(const float* scores, int64_t score_cols, const in
                                int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                                int32_t* status, void* workspace, hipStream_t stream);
 
+// One-workgroup-per-row selector over the rows whose row_flag is nonzero
+// only (the others are left untouched): the fused path's fallback.
+hipError_t launch_select_flagged(const float* scores, int64_t score_cols, const int32_t* pos,
+                                 int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
+                                 int32_t* status, const int32_t* row_flag, hipStream_t stream);
+
+// Ring scorer jobs (score.hip): prepared queries in groups of kRingRows rows,
+// pooled keys streamed through LDS.  Column j of a row scores the pooled key
+// of block j * bstride; row r has ceil(((pos[r] + 1) / 4) / bstride) columns.
+// With cand == NULL the scores go to scores[r * score_cols + j].  Otherwise
+// nothing is stored but the blocks whose head sum (the score before its final
+// scale 0.5 / sqrt(128)) has bits >= thr[r], as (sum bits, block) entries in
+// cand[((r * splits + split) * 4 + g) * cap + e], e < cap, where g = (block
+// % 32) / 8, with the per-region totals in cnt[(r * splits + split) * 4 + g].
+// group_flag, when set, restricts the job to row groups whose flag is nonzero.
+constexpr int kRingRows = 128;
+struct RingJob {
+  const uint16_t* qhat;
+  const int32_t* pos;
+  int64_t rows;
+  const uint16_t* pooled;
+  int64_t tokens;
+  int bstride;
+  float* scores;
+  int64_t score_cols;
+  int32_t* status;
+  const int32_t* group_flag;
+  const uint32_t* thr;  // padded to a multiple of kRingRows rows
+  uint2* cand;
+  int32_t* cnt;
+  int cap;
+};
+// splits per row group of a job over `cols` columns with `target` workgroups
+int64_t ring_splits(int64_t rows, int64_t cols, int64_t target);
+hipError_t launch_ring(const RingJob& j, int64_t target, hipStream_t stream);
+
+// Fused score -> select for prefill batches (fused.hip).
+int64_t score_select_workspace_bytes(int64_t rows, int64_t tokens, int keep_max);
+hipError_t launch_score_select(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                               const uint16_t* pooled, int64_t tokens, int keep_max,
+                               uint8_t* mask, int32_t* status, void* workspace,
+                               hipStream_t stream);
+
 }  // namespace qsa

@@ -28,6 +28,8 @@
 // for its own tile's loads, not for the stores issued after them.
 // A workgroup walks a contiguous range of block tiles and stops at the
 // largest visible block count of its rows (causal prefill rows are ragged).
+#include <utility>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -36,10 +38,10 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreThreads = 256;
 constexpr int kPitch = 136;  // prologue LDS row pitch in bf16 elements (272 bytes)
-constexpr float kScale = static_cast<float>(0.088388347648318440550);  // 1/sqrt(128)
 constexpr int kStoreNT = 2;  // buffer-store cache policy: nt
 
 struct ScoreArgs {
@@ -503,9 +505,15 @@ struct RingArgs {
   int64_t rows;
   const uint16_t* pooled;
   int64_t tokens;
+  int bstride;  // column j scores the pooled key of block j * bstride
   float* scores;
   int64_t score_cols;
-  int32_t* status;
+  int32_t* status;              // may be null: bad positions are then not flagged
+  const int32_t* group_flag;    // non-null: only row groups with a nonzero flag run
+  const uint32_t* thr;          // EMIT: per-row thresholds (head-sum bits), 128-row padded
+  uint2* cand;                  // EMIT: [rows][splits][4][cap] (sum bits, block)
+  int32_t* cnt;                 // EMIT: [rows][splits][4] blocks at or above the threshold
+  int cap;
   int splits;  // workgroups per row group; split s takes tiles s, s + splits, ...
   int tasks;
 };
@@ -529,6 +537,11 @@ __device__ __forceinline__ void lds_wait8(bf16x8_t (&b)[8]) {
                :
                : "memory");
 }
+// One LDS word written at addr + OFF, as inline assembly (no wait).
+template <int OFF>
+__device__ __forceinline__ void lds_write_word(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
+}
 // One LDS word read and its wait, as inline assembly.
 __device__ __forceinline__ int lds_read_word(uint32_t addr) {
   int v;
@@ -539,22 +552,46 @@ __device__ __forceinline__ int lds_read_word(uint32_t addr) {
 // Score of query row (q4 of the lane's accumulator rows) from its four head
 // dot products: relu(d) = (d + |d|) / 2 exactly (NaN stays NaN), so the head
 // sum of the doubled terms times scale / 2 is the f32 score.
-__device__ __forceinline__ float pair_score(const f32x16_t& acc, int q4) {
+// pair_sum is the head sum before the final scale: the score is exactly
+// pair_sum * (0.5 * scale) rounded once, a non-decreasing function of it.
+__device__ __forceinline__ float pair_sum(const f32x16_t& acc, int q4) {
   const float h0 = acc[4 * q4 + 0], h1 = acc[4 * q4 + 1];
   const float h2 = acc[4 * q4 + 2], h3 = acc[4 * q4 + 3];
   float s = (h0 + fabsf(h0)) + (h1 + fabsf(h1));
   s = s + (h2 + fabsf(h2));
   s = s + (h3 + fabsf(h3));
-  return s * (0.5f * kScale);
+  return s;
+}
+__device__ __forceinline__ float pair_score(const f32x16_t& acc, int q4) {
+  return pair_sum(acc, q4) * (0.5f * kScale);
 }
 
-template <int WM>
+// EMIT: instead of storing the scores, the kernel keeps the blocks whose head
+// sum (pair_sum, the score before its final scale), read as an unsigned
+// integer, is at least the row's threshold thr[row] (given in the sum
+// domain).  Sums are never negative (relu terms), so this is their order, and
+// NaN / +-Inf bits lie above every threshold up to +Inf: non-finite scores are
+// always kept, for the selector to refuse.  Each epilogue phase (16 rows x 32
+// blocks of a wave) goes through a small LDS tile so that lane l owns row
+// l / 4 of the phase and blocks 8 (l % 4) .. + 7 of the tile: its threshold
+// and its running count stay in the lane, and a kept block is one compare and
+// one store, with no cross-lane work.  Kept blocks go to the region of (row,
+// split, l % 4), cap entries of (sum bits, block); the counts, which may
+// exceed cap (the excess overwrote the region's last entry), finally go to
+// cnt[row][split][l % 4].
+template <int WM, bool EMIT>
 __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   using G = RingGeom<WM>;
   constexpr int RG = G::RG, TILE = G::TILE, STAGE = G::STAGE, kL = G::kL, kStores = G::kStores, D = G::D;
+  static_assert(!EMIT || WM == 4, "emission assumes 32 rows per wave, 32 blocks per step");
   __shared__ __attribute__((aligned(16))) unsigned char ring[D * STAGE];
   __shared__ int nvis[RG];
   __shared__ int sh_nmax, sh_nmin;
+  // EMIT: per-row thresholds, and one 16 x 32 sum tile per wave (row pitch
+  // 36 words keeps 16-byte reads aligned)
+  constexpr int kEPitch = 36;
+  __shared__ uint32_t sthr[EMIT ? RG : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t etile[EMIT ? 4 * 16 * kEPitch : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = wave % WM;   // 32-row slice of the group
@@ -568,9 +605,20 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   }
   const int rg = task / a.splits;
   const int split = task - rg * a.splits;
+  if (a.group_flag != nullptr && a.group_flag[rg] == 0) return;  // uniform
   const int64_t row0 = static_cast<int64_t>(rg) * RG;
   const int blk_begin = split * TILE;
   const int stride = a.splits * TILE;
+
+  // EMIT: lane l's rows are 32 m + l / 4 (phase of acc[0..1]) and 32 m + 16 +
+  // l / 4 (acc[2..3]); its blocks of a tile are 8 (l % 4) .. + 7
+  const int er = lane >> 2, cg = lane & 3;
+  uint32_t ecnt0 = 0u, ecnt1 = 0u;
+  auto store_counts = [&]() {
+    const int64_t r0 = row0 + 32 * m + er, r1 = r0 + 16;
+    if (r0 < a.rows) a.cnt[(r0 * a.splits + split) * 4 + cg] = static_cast<int32_t>(ecnt0);
+    if (r1 < a.rows) a.cnt[(r1 * a.splits + split) * 4 + cg] = static_cast<int32_t>(ecnt1);
+  };
 
   // A fragments: subtile ms = rows 32 m + 8 ms .. + 7 as 32 M-rows (row, head)
   bf16x8_t afrag[4][8];
@@ -585,7 +633,10 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       for (int ks = 0; ks < 8; ++ks) afrag[ms][ks] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ks);
     }
   }
-  // visible block counts (wave 0, lane l: rows l and l + 64)
+  if constexpr (EMIT)
+    if (tid < RG) sthr[tid] = a.thr[row0 + tid];
+  // visible columns (wave 0, lane l: rows l and l + 64): blocks (p + 1) / 4,
+  // of which every bstride-th is a column
   if (wave == 0) {
     uint32_t mx = 0u, mn = 0x7FFFFFFFu;
 #pragma unroll
@@ -597,8 +648,8 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
         if (r < a.rows) {
           const int p = a.pos[r];
           if (p >= 0 && p < a.tokens)
-            n = (p + 1) / kRatio;
-          else if (split == 0)
+            n = ((p + 1) / kRatio + a.bstride - 1) / a.bstride;
+          else if (split == 0 && a.status != nullptr)
             atomicOr(a.status, 1);
         }
         nvis[lr] = n;
@@ -615,14 +666,18 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   }
   __syncthreads();
   const int nmax = sh_nmax;
-  const int nmin = sh_nmin;  // blocks every row of the workgroup sees
-  if (blk_begin >= nmax) return;  // uniform; nothing in flight
+  const int nmin = sh_nmin;  // columns every row of the workgroup sees
+  if (blk_begin >= nmax) {   // uniform; nothing in flight
+    if constexpr (EMIT) store_counts();
+    return;
+  }
 
   // ---- key ring.  Load i of wave w fills tile rows 4 (w kL + i) + lane / 16
   // with the key's 16-byte chunk (lane % 16) ^ (row & 7) at chunk lane % 16,
   // so a B-fragment read (32 rows, one chunk each) spreads over all banks.
+  const int kbytes = 256 * a.bstride;  // bytes from one column's key to the next
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.pooled), static_cast<short>(0), nmax * 256, 0x00020000);
+      const_cast<uint16_t*>(a.pooled), static_cast<short>(0), nmax * kbytes, 0x00020000);
   const int lrow = lane >> 4, lchunk = lane & 15;
   auto load_tile = [&](int nb0, int stage) {
 #pragma unroll
@@ -630,7 +685,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       const int row = 4 * (wave * kL + i) + lrow;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           krsrc, (__attribute__((address_space(3))) void*)(ring + stage * STAGE + 1024 * (wave * kL + i)), 16,
-          row * 256 + 16 * (lchunk ^ (row & 7)), nb0 * 256, 0, 0);
+          row * kbytes + 16 * (lchunk ^ (row & 7)), nb0 * kbytes, 0, 0);
     }
   };
 #pragma unroll
@@ -649,9 +704,10 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   // subtile ms writes row 32 m + 8 ms + 2 q4 + h, column nb0 + col.  An
   // offset past the resource drops the store (blocks outside a row's prefix).
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-      a.scores + row0 * a.score_cols, static_cast<short>(0), static_cast<int>(RG * a.score_cols * 4), 0x00020000);
-  const int vbase = ((32 * m + h) * static_cast<int>(a.score_cols) + col) * 4;
-  const int rowbytes = static_cast<int>(a.score_cols) * 4;
+      EMIT ? nullptr : a.scores + row0 * a.score_cols, static_cast<short>(0),
+      EMIT ? 0 : static_cast<int>(RG * a.score_cols * 4), 0x00020000);
+  const int vbase = EMIT ? 0 : ((32 * m + h) * static_cast<int>(a.score_cols) + col) * 4;
+  const int rowbytes = EMIT ? 0 : static_cast<int>(a.score_cols) * 4;
   constexpr int kDrop = static_cast<int>(0x80000000u);
 
   auto pair_store = [&](const f32x16_t& x0, const f32x16_t& x1, int m0, int nb0, bool live, bool fast) {
@@ -672,6 +728,71 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[j]), orsrc, off,
                                             (8 * ms + 2 * q4) * rowbytes + 4 * nb0, 0);
     }
+  };
+
+  // EMIT: regions of the group's rows, [row][split][4][cap]
+  const int crow = EMIT ? a.splits * 4 * a.cap * 8 : 0;  // bytes of one row's regions
+  const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+      EMIT ? a.cand + row0 * a.splits * 4 * a.cap : nullptr, static_cast<short>(0), RG * crow, 0x00020000);
+  const int ebase = EMIT ? (32 * m + er) * crow + (split * 4 + cg) * a.cap * 8 : 0;
+  const uint32_t capm1 = EMIT ? static_cast<uint32_t>(a.cap - 1) : 0u;
+  const uint32_t etile_w = lds_addr(etile) + 4 * (wave * 16 * kEPitch);
+  const uint32_t ewrite = etile_w + 4 * (h * kEPitch + r);        // lane (r, h) writes
+  const uint32_t eread = etile_w + 4 * (er * kEPitch + 8 * cg);   // lane l reads
+  auto pair_emit = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast) {
+    constexpr int m0 = decltype(m0c)::value;
+    // the phase's sums into the wave's tile: slot (ms, q4) of lane (r, h) is
+    // tile row 8 (ms - m0) + 2 q4 + h, column r
+    lds_write_word<4 * 0 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 0)));
+    lds_write_word<4 * 2 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 1)));
+    lds_write_word<4 * 4 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 2)));
+    lds_write_word<4 * 6 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 3)));
+    lds_write_word<4 * 8 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 0)));
+    lds_write_word<4 * 10 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 1)));
+    lds_write_word<4 * 12 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 2)));
+    lds_write_word<4 * 14 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 3)));
+    // lane l: its row's threshold and visible blocks, and its 8 sums
+    const uint32_t prow = 32 * m + 8 * m0 + er;  // group row
+    uint32_t t, nv;
+    u32x4_t sums;
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b32 %1, %4\n\t"
+        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(sums), "=v"(t), "=v"(nv)
+        : "v"(eread), "v"(lds_addr(sthr) + 4 * prow), "v"(lds_addr(nvis) + 4 * prow)
+        : "memory");
+    u32x4_t sums2;
+    asm volatile("ds_read_b128 %0, %1 offset:16\n\ts_waitcnt lgkmcnt(0)" : "=v"(sums2) : "v"(eread) : "memory");
+    const uint32_t blk0 = static_cast<uint32_t>(nb0 + 8 * cg);
+    uint32_t& cnt = m0 == 0 ? ecnt0 : ecnt1;
+    const int soff = m0 == 0 ? 0 : 16 * crow;
+    // each path issues exactly 8 stores (the ring's vmcnt accounting)
+    auto emit8 = [&](auto visc) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t v = j < 4 ? sums[j] : sums2[j - 4];
+        const uint32_t blk = blk0 + j;
+        bool c = v >= t;
+        if constexpr (decltype(visc)::value) c = c & live & (blk < nv);
+        const uint32_t slot = cnt < capm1 ? cnt : capm1;  // past capacity: the row falls back
+        const int voff = c ? ebase + 8 * static_cast<int>(slot) : kDrop;
+        __attribute__((ext_vector_type(2))) uint32_t e = {v, blk};
+        __builtin_amdgcn_raw_buffer_store_b64(e, crsrc, voff, soff, 0);
+        cnt += c ? 1u : 0u;
+      }
+    };
+    if (fast)  // every block of the tile visible to every row of the group
+      emit8(std::integral_constant<bool, false>{});
+    else
+      emit8(std::integral_constant<bool, true>{});
+  };
+  auto epilogue = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast) {
+    if constexpr (EMIT)
+      pair_emit(x0, x1, m0c, nb0, live, fast);
+    else
+      pair_store(x0, x1, decltype(m0c)::value, nb0, live, fast);
   };
 
   f32x16_t acc[4];
@@ -704,7 +825,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       bf[7] = lds_read16<128>(b3);
     }
     // phase A: the previous step's acc[2..3] (dropped in the first step)
-    pair_store(acc[2], acc[3], 2, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin);
+    epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin);
     lds_wait8(bf);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -717,11 +838,12 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
       acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
     }
-    pair_store(acc[0], acc[1], 0, nb0, true, nb0 + TILE <= nmin);
+    epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin);
     // Tile t + 1 has landed once at most N of this wave's memory operations
     // are outstanding, N = what was issued after its loads: the loads of
-    // (D - 2) tiles and the 16 stores of each step since (D - 1 steps in the
+    // (D - 2) tiles and the stores of each step since (D - 1 steps in the
     // steady state, step + 1 in the first D - 2 steps).  Smaller N is safe.
+    // Both epilogues issue kStores stores per step, whatever they keep.
     {
       constexpr int NA0 = (D - 2) * kL + (D - 1) * kStores;
       constexpr int NA = NA0 > 63 ? 63 : NA0;
@@ -740,35 +862,33 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
     ++step;
     stage = stage + 1 == D ? 0 : stage + 1;
   }
-  pair_store(acc[2], acc[3], 2, prev_nb0, true, prev_nb0 + TILE <= nmin);
+  epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, true, prev_nb0 + TILE <= nmin);
+  if constexpr (EMIT) store_counts();
   wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
 // Workgroups: `target` in all, at least one tile each; a row group's splits
 // take interleaved tiles.
-template <int WM>
-hipError_t launch_score_ring_geom(const ScoreArgs& base, int64_t target, hipStream_t stream) {
-  using G = RingGeom<WM>;
-  RingArgs a{};
-  a.qhat = base.qhat;
-  a.pos = base.pos;
-  a.rows = base.rows;
-  a.pooled = base.pooled;
-  a.tokens = base.tokens;
-  a.scores = base.scores;
-  a.score_cols = base.score_cols;
-  a.status = base.status;
-  const int64_t nb_total = a.tokens / kRatio;
-  const int64_t row_groups = (a.rows + G::RG - 1) / G::RG;
-  int64_t n_tiles = (nb_total + G::TILE - 1) / G::TILE;
+int64_t ring_splits_for(int64_t row_groups, int64_t cols, int tile, int64_t target) {
+  int64_t n_tiles = (cols + tile - 1) / tile;
   if (n_tiles < 1) n_tiles = 1;
   int64_t splits = (target + row_groups - 1) / row_groups;
   if (splits < 1) splits = 1;
   if (splits > n_tiles) splits = n_tiles;
+  return splits;
+}
+
+template <int WM, bool EMIT>
+hipError_t launch_score_ring_geom(RingArgs a, int64_t target, hipStream_t stream) {
+  using G = RingGeom<WM>;
+  const int64_t nb_total = a.tokens / kRatio;
+  const int64_t cols = (nb_total + a.bstride - 1) / a.bstride;
+  const int64_t row_groups = (a.rows + G::RG - 1) / G::RG;
+  const int64_t splits = ring_splits_for(row_groups, cols, G::TILE, target);
   if (row_groups * splits > 0x7FFFFFFF) return hipErrorInvalidValue;
   a.splits = static_cast<int>(splits);
   a.tasks = static_cast<int>(row_groups * splits);
-  score_ring_kernel<WM><<<dim3(static_cast<unsigned>(a.tasks)), dim3(256), 0, stream>>>(a);
+  score_ring_kernel<WM, EMIT><<<dim3(static_cast<unsigned>(a.tasks)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -777,8 +897,18 @@ bool ring_fits(const ScoreArgs& a, int rows_per_group) {
   return a.score_cols <= 0x7FFFFFFF / (4 * rows_per_group);
 }
 
-hipError_t launch_score_ring(const ScoreArgs& a, hipStream_t stream) {
-  return launch_score_ring_geom<4>(a, 1024, stream);
+hipError_t launch_score_ring(const ScoreArgs& s, hipStream_t stream) {
+  RingArgs a{};
+  a.qhat = s.qhat;
+  a.pos = s.pos;
+  a.rows = s.rows;
+  a.pooled = s.pooled;
+  a.tokens = s.tokens;
+  a.bstride = 1;
+  a.scores = s.scores;
+  a.score_cols = s.score_cols;
+  a.status = s.status;
+  return launch_score_ring_geom<4, false>(a, 1024, stream);
 }
 
 template <int WM, int MS, int D, bool PREP>
@@ -826,6 +956,30 @@ hipError_t launch_score_rows(const ScoreArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t ring_splits(int64_t rows, int64_t cols, int64_t target) {
+  return ring_splits_for((rows + kRingRows - 1) / kRingRows, cols, 32, target);
+}
+
+hipError_t launch_ring(const RingJob& j, int64_t target, hipStream_t stream) {
+  RingArgs a{};
+  a.qhat = j.qhat;
+  a.pos = j.pos;
+  a.rows = j.rows;
+  a.pooled = j.pooled;
+  a.tokens = j.tokens;
+  a.bstride = j.bstride;
+  a.scores = j.scores;
+  a.score_cols = j.score_cols;
+  a.status = j.status;
+  a.group_flag = j.group_flag;
+  a.thr = j.thr;
+  a.cand = j.cand;
+  a.cnt = j.cnt;
+  a.cap = j.cap;
+  if (j.cand != nullptr) return launch_score_ring_geom<4, true>(a, target, stream);
+  return launch_score_ring_geom<4, false>(a, target, stream);
+}
 
 hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
                         const uint16_t* w, const RopeParams& rp, const uint16_t* pooled,

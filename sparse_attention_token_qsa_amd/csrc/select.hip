@@ -51,6 +51,7 @@ struct SelectArgs {
   int32_t* idx;        // index mode: [rows, idx_stride] kept token indices
   int64_t idx_stride;
   int32_t* counts;     // index mode: [rows] entries written
+  const int32_t* row_flag;  // non-null: only rows with a nonzero flag are selected
 };
 
 // IDX: instead of the mask, row r's kept token indices in ascending order
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t row = blockIdx.x;
+  if (a.row_flag != nullptr && a.row_flag[row] == 0) return;  // uniform
   const int64_t T = a.tokens;
   uint8_t* mrow = a.mask + row * T;
   const int64_t p = a.pos[row];
@@ -388,6 +390,23 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
   a.mask = mask;
   a.status = status;
   // 16-byte loads of 4 scores and 16-byte mask stores of 4 blocks
+  const bool vec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0) &&
+                   (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
+  return launch_select_rows<false>(a, rows, vec, stream);
+}
+
+hipError_t launch_select_flagged(const float* scores, int64_t score_cols, const int32_t* pos,
+                                 int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
+                                 int32_t* status, const int32_t* row_flag, hipStream_t stream) {
+  SelectArgs a{};
+  a.scores = scores;
+  a.score_cols = score_cols;
+  a.pos = pos;
+  a.tokens = tokens;
+  a.keep_max = keep_max;
+  a.mask = mask;
+  a.status = status;
+  a.row_flag = row_flag;
   const bool vec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0) &&
                    (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
   return launch_select_rows<false>(a, rows, vec, stream);

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 4
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 5
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -213,6 +213,50 @@ def test_select_ws_refusals(lib):
     assert select_ws(lib, scores_len=8 * 16385 - 1) == CAP
     assert select_ws(lib, ws_bytes=8 * 5 * (4096 + 256) - 1) == CAP
     assert select_ws(lib, ws=P + 8) == PARAM
+
+
+def fused(lib, **kw):
+    a = dict(qhat=P, pos=P, rows=8, pooled=P, tokens=4096, budget=2048, mask=P, status=P, ws=0x100000,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.qsa_score_select_mask(a["qhat"], a["pos"], a["rows"], a["pooled"], a["tokens"], a["budget"],
+                                     a["mask"], a["status"], a["ws"], a["ws_bytes"], None)
+
+
+def test_score_select_workspace_sizes(lib):
+    assert lib.qsa_score_select_workspace_bytes(0, 65536, 2048) == 0
+    assert lib.qsa_score_select_workspace_bytes(8, 0, 2048) == 0
+    big = lib.qsa_score_select_workspace_bytes(8192, 65536, 2048)
+    # at least the fallback score matrix and the sampled scores
+    assert big >= 8192 * 16384 * 4 + 8192 * 1024 * 4
+    assert big < 1 << 30
+    assert lib.qsa_score_select_workspace_bytes(8, 64, 4) > 0
+    assert lib.qsa_score_select_workspace_bytes(8, 64, 4) % 256 == 0
+    assert lib.qsa_score_select_workspace_bytes(-1, 64, 4) == EXTENT
+    assert lib.qsa_score_select_workspace_bytes(8, -1, 4) == EXTENT
+    assert lib.qsa_score_select_workspace_bytes(8, 64, 6) == BUDGET
+    assert lib.qsa_score_select_workspace_bytes(8, 64, 2052) == BUDGET
+    assert lib.qsa_score_select_workspace_bytes(8, 262148, 4) == CAP
+    assert lib.qsa_score_select_workspace_bytes(2**31, 64, 4) == CAP
+
+
+def test_score_select_refusals(lib):
+    assert fused(lib, rows=0) == OK
+    assert fused(lib, tokens=0) == OK
+    assert fused(lib, rows=0, qhat=None, pos=None, mask=None, status=None, ws=None) == OK
+    for k in ("qhat", "pos", "pooled", "mask", "status", "ws"):
+        assert fused(lib, **{k: None}) == NULL, k
+    assert fused(lib, tokens=3, pooled=None, ws_bytes=0) != NULL  # no complete block: no pooled keys read
+    assert fused(lib, rows=-1) == EXTENT
+    assert fused(lib, tokens=-1) == EXTENT
+    assert fused(lib, ws_bytes=-1) == EXTENT
+    for b in (0, -4, 2, 2052):
+        assert fused(lib, budget=b) == BUDGET, b
+    assert fused(lib, tokens=262148) == CAP
+    assert fused(lib, rows=2**31) == CAP
+    need = lib.qsa_score_select_workspace_bytes(8, 4096, 2048)
+    assert fused(lib, ws_bytes=need - 1) == CAP
+    assert fused(lib, ws=0x100000 + 16, ws_bytes=need) == PARAM
 
 
 def prep(lib, **kw):
