@@ -37,6 +37,7 @@ MAX_KEEP_BLOCKS = 512
 
 STATUS_BAD_POSITION = 1
 STATUS_NONFINITE_SCORE = 2
+STATUS_BAD_INDEX = 4
 
 
 # ----------------------------------------------------------------------------
@@ -362,6 +363,74 @@ def select_indices(scores: np.ndarray, score_cols: int, pos: np.ndarray, tokens:
         idx[r], counts[r], st = select_indices_row(row, int(pos[r]), tokens, budget)
         status |= st
     return idx, counts, status
+
+
+# ----------------------------------------------------------------------------
+# Decode K/V gather
+# ----------------------------------------------------------------------------
+
+def gather_kv(k_cache, v_cache, page_size: int, page_table, table_stride: int,
+              table_len: int, idx, idx_stride: int, counts, rows: int, slots: int):
+    """The selected tokens' K and V vectors copied out of a paged cache into
+    contiguous per-row scratch, and the identity page table over it.
+
+    [QSA] module notes and decode_select: the kept token list (ascending kept
+    blocks' tokens, then the tail) indexes the sequence's paged K/V cache;
+    each listed token's vector is copied, in list order, into a contiguous
+    NHD scratch, which the paged decode attention then reads through an
+    identity block table of ceil(n_sel / block_size) pages with sequence
+    length n_sel.
+
+    Readings where the page is silent, one row per sequence (rows may share
+    a cache):
+      - cache layout [n_pages, page_size, kv_dim] (page, slot, then the
+        kv_heads x head_dim vector), token t of row r at page
+        page_table[r * table_stride + t // page_size], slot t % page_size;
+        table_stride 0 shares one table;
+      - row r's scratch holds `slots` (a multiple of page_size) entries:
+        entry i < counts[r] is token idx[r * idx_stride + i], the rest zero;
+      - the identity table presents all rows' scratch as one paged pool:
+        row r's page j is pool page r * (slots / page_size) + j;
+      - a token index that is negative, at or past table_len * page_size, or
+        whose page lies outside the cache is written as zeros and sets
+        STATUS_BAD_INDEX; so does a count outside [0, slots], clamped there.
+
+    k_cache, v_cache: [n_pages, page_size, kv_dim] uint16 (bf16 bits).
+    Returns (k_out, v_out [rows, slots, kv_dim] uint16, table [rows,
+    slots // page_size] int32, status).
+    """
+    k_cache = np.asarray(k_cache, dtype=np.uint16)
+    v_cache = np.asarray(v_cache, dtype=np.uint16)
+    n_pages, ps, kv_dim = k_cache.shape
+    assert ps == page_size and slots % page_size == 0
+    page_table = np.asarray(page_table, dtype=np.int64).reshape(-1)
+    idx = np.asarray(idx, dtype=np.int64).reshape(-1)
+    counts = np.asarray(counts, dtype=np.int64).reshape(-1)
+    k_out = np.zeros((rows, slots, kv_dim), dtype=np.uint16)
+    v_out = np.zeros((rows, slots, kv_dim), dtype=np.uint16)
+    ppr = slots // page_size
+    table = np.zeros((rows, ppr), dtype=np.int32)
+    status = 0
+    for r in range(rows):
+        for j in range(ppr):
+            table[r, j] = r * ppr + j
+        c = int(counts[r])
+        if c < 0 or c > slots:
+            status |= STATUS_BAD_INDEX
+            c = min(max(c, 0), slots)
+        for i in range(c):
+            t = int(idx[r * idx_stride + i])
+            lp = t // page_size if t >= 0 else -1
+            if t < 0 or lp >= table_len:
+                status |= STATUS_BAD_INDEX
+                continue
+            page = int(page_table[r * table_stride + lp])
+            if page < 0 or page >= n_pages:
+                status |= STATUS_BAD_INDEX
+                continue
+            k_out[r, i] = k_cache[page, t % page_size]
+            v_out[r, i] = v_cache[page, t % page_size]
+    return k_out, v_out, table, status
 
 
 # ----------------------------------------------------------------------------

@@ -542,3 +542,105 @@ def test_select_indices_refusals_and_format_faults():
     for name, (row, cnt) in bad.items():
         with pytest.raises(AssertionError):
             check_index_list(row, cnt, mask[0], 2054, 2048)
+
+
+# ---------------------------------------------------------------- K/V gather
+
+def encoded_cache(n_pages, page_size, kv_dim, page_of_logical, salt):
+    """A paged cache whose vector for token t carries t in its first three
+    elements (base-256 digits, exact in bf16) and `salt` in the fourth, the
+    rest a fixed pattern; page_of_logical maps logical page -> physical."""
+    k = np.zeros((n_pages, page_size, kv_dim), dtype=np.uint16)
+    for lp, pp in enumerate(page_of_logical):
+        for s in range(page_size):
+            t = lp * page_size + s
+            digits = np.array([t & 255, (t >> 8) & 255, (t >> 16) & 255, salt], dtype=np.float32)
+            k[pp, s, :4] = O.bf16_from_f32(digits)
+            k[pp, s, 4:] = O.bf16_from_f32(np.float32(0.5))
+    return k
+
+
+def decode_token(vec):
+    d = O.f32_from_bf16(vec[:4]).astype(np.int64)
+    return int(d[0] + 256 * d[1] + 65536 * d[2]), int(d[3])
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_gather_returns_each_listed_token_through_the_page_table(shared):
+    """Every gathered vector decodes to the token the list names (K salt 1,
+    V salt 2), in list order, whatever physical page holds it; entries past
+    the count are zero; the identity table is row-major over the scratch."""
+    rng = np.random.default_rng(11)
+    page_size, kv_dim, rows, slots = 16, 24, 3, 48
+    n_log = 40
+    perm = rng.permutation(n_log + 7)[:n_log]  # physical pages, 7 unused
+    kc = encoded_cache(n_log + 7, page_size, kv_dim, perm, 1)
+    vc = encoded_cache(n_log + 7, page_size, kv_dim, perm, 2)
+    if shared:
+        table, tstride = perm.astype(np.int32), 0
+    else:
+        # row r's sequence is the shared one shifted by r pages
+        table = np.concatenate([np.roll(perm, -r) for r in range(rows)]).astype(np.int32)
+        tstride = n_log
+    idx_stride = 50
+    idx = np.full((rows, idx_stride), -1, np.int32)
+    counts = np.array([45, 0, 17], np.int32)
+    for r in range(rows):
+        pick = np.sort(rng.choice(n_log * page_size, counts[r], replace=False))
+        idx[r, : counts[r]] = pick
+    ko, vo, tab, st = O.gather_kv(kc, vc, page_size, table, tstride, n_log, idx, idx_stride, counts,
+                                  rows, slots)
+    assert st == 0
+    for r in range(rows):
+        for i in range(slots):
+            if i < counts[r]:
+                t = int(idx[r, i])
+                shift = 0 if shared else r * page_size
+                want = (t + shift) % (n_log * page_size)
+                assert decode_token(ko[r, i]) == (want, 1), (r, i)
+                assert decode_token(vo[r, i]) == (want, 2), (r, i)
+            else:
+                assert not ko[r, i].any() and not vo[r, i].any()
+        assert np.array_equal(tab[r], r * (slots // page_size) + np.arange(slots // page_size))
+
+
+def test_gather_with_identity_paging_is_plain_indexing():
+    """With physical page = logical page, the gather is numpy indexing of the
+    flattened cache."""
+    rng = np.random.default_rng(12)
+    page_size, kv_dim, n_pages, rows, slots = 8, 16, 30, 4, 64
+    kc = rng.integers(0, 1 << 16, size=(n_pages, page_size, kv_dim), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=(n_pages, page_size, kv_dim), dtype=np.uint16)
+    counts = rng.integers(0, slots + 1, size=rows).astype(np.int32)
+    idx = np.full((rows, slots), -1, np.int32)
+    for r in range(rows):
+        idx[r, : counts[r]] = np.sort(rng.choice(n_pages * page_size, counts[r], replace=False))
+    ko, vo, _, st = O.gather_kv(kc, vc, page_size, np.arange(n_pages, dtype=np.int32), 0, n_pages, idx,
+                                slots, counts, rows, slots)
+    assert st == 0
+    flat_k, flat_v = kc.reshape(-1, kv_dim), vc.reshape(-1, kv_dim)
+    for r in range(rows):
+        c = counts[r]
+        assert np.array_equal(ko[r, :c], flat_k[idx[r, :c]])
+        assert np.array_equal(vo[r, :c], flat_v[idx[r, :c]])
+
+
+def test_gather_bad_indices_and_counts_write_zeros_and_flag():
+    page_size, kv_dim = 4, 8
+    kc = np.full((3, page_size, kv_dim), 7, np.uint16)
+    vc = np.full((3, page_size, kv_dim), 9, np.uint16)
+    table = np.array([2, 5, 0], np.int32)  # logical page 1 -> physical 5: outside the cache
+    idx = np.array([[0, -3, 5, 11, 12, 3, 0, 0]], np.int32)
+    ko, vo, _, st = O.gather_kv(kc, vc, page_size, table, 0, 3, idx, 8, np.array([6]), 1, 8)
+    assert st == O.STATUS_BAD_INDEX
+    good = [0, 3, 5]  # entries 0 (t 0), 3 (t 11, page 0), 5 (t 3)
+    for i in range(8):
+        if i in good:
+            assert np.all(ko[0, i] == 7) and np.all(vo[0, i] == 9)
+        else:
+            assert not ko[0, i].any() and not vo[0, i].any(), i
+    for bad_count in (-1, 9):
+        ko, _, _, st = O.gather_kv(kc, vc, page_size, table, 0, 3, np.zeros((1, 8), np.int32), 8,
+                                   np.array([bad_count]), 1, 8)
+        assert st == O.STATUS_BAD_INDEX
+        assert np.all(ko[0, :8 if bad_count > 0 else 0] == 7) and not ko[0, 8:].any()
