@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 5
+#define QSA_ABI_VERSION 6
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -57,6 +57,7 @@ extern "C" {
 /* Bits OR-ed into *dev_status by the kernels. */
 #define QSA_STATUS_BAD_POSITION 1   /* pos[r] outside [0, tokens) */
 #define QSA_STATUS_NONFINITE_SCORE 2 /* a NaN or +-Inf among a row's visible block scores */
+#define QSA_STATUS_BAD_INDEX 4       /* qsa_gather_kv: a token outside the cache, or a bad count */
 
 /*
  * qsa_pool_keys -- pooled key of every 4-token block in
@@ -283,6 +284,51 @@ int qsa_score_select_mask(const uint16_t* qhat, const int32_t* pos, int64_t rows
                           const uint16_t* pooled, int64_t tokens, int64_t budget, uint8_t* mask,
                           int32_t* dev_status, void* workspace, int64_t workspace_bytes,
                           void* stream);
+
+/*
+ * qsa_gather_kv -- each row's selected tokens' K and V vectors, copied from a
+ * paged cache into contiguous per-row scratch, with the identity page table
+ * that presents the scratch as a paged cache.
+ *
+ * [QSA] module notes and decode_select: decode selection gathers the kept
+ * tokens' K/V into a contiguous NHD scratch that the paged decode attention
+ * reads through an identity block table (ceil(n_sel / block_size) pages,
+ * sequence length n_sel).  The token lists are qsa_select_indices' output.
+ *
+ *   k_cache, v_cache  [n_pages, page_size, kv_dim] bf16, dense: page, slot,
+ *                     then the kv_heads x head_dim vector (kv_dim elements).
+ *   page_table        int32; token t of row r lives at page
+ *                     page_table[r * table_stride + t / page_size], slot t %
+ *                     page_size, for t / page_size < table_len.
+ *                     table_stride 0: one table for every row.
+ *   idx, idx_stride, counts   row r's list: idx[r * idx_stride + i], i <
+ *                     counts[r] (as qsa_select_indices writes them).
+ *   slots             entries per row of the scratch, a multiple of
+ *                     page_size (>= the longest list: budget + 3 rounded up).
+ *   k_out, v_out      [rows, slots, kv_dim] bf16: entry i < counts[r] is the
+ *                     listed token's vector, every other entry zero.
+ *   out_table         [rows, slots / page_size] int32: row r's page j is
+ *                     page r * (slots / page_size) + j of k_out / v_out
+ *                     viewed as [rows * slots / page_size, page_size, kv_dim];
+ *                     the row's sequence length is counts[r].
+ *   dev_status        a token index that is negative, at or past table_len *
+ *                     page_size, or whose page lies outside [0, n_pages), is
+ *                     written as zeros; a count outside [0, min(slots,
+ *                     idx_stride)] is clamped into it; both set
+ *                     QSA_STATUS_BAD_INDEX.
+ * Refusals: QSA_ERR_EXTENT (negative n_pages, table_len, table_stride,
+ * idx_stride, rows or slots), QSA_ERR_PARAM (page_size or kv_dim < 1, slots
+ * not a multiple of page_size), QSA_ERR_STRIDE (0 < table_stride <
+ * table_len), QSA_ERR_CAPACITY (a buffer extent overflows, or
+ * rows * slots / 4 > INT32_MAX), QSA_ERR_NULL (a pointer the extents make
+ * necessary is NULL).  rows == 0 or slots == 0: QSA_OK, nothing enqueued.
+ */
+int qsa_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_pages,
+                  int32_t page_size, int32_t kv_dim, const int32_t* page_table,
+                  int64_t table_stride, int64_t table_len, const int32_t* idx,
+                  int64_t idx_stride, const int32_t* counts, int64_t rows, int64_t slots,
+                  uint16_t* k_out, uint16_t* v_out, int32_t* out_table, int32_t* dev_status,
+                  void* stream);
 
 /*
  * qsa_rope_inv_freq -- host only: the rotary frequencies the kernels use,

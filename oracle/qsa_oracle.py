@@ -393,7 +393,8 @@ def gather_kv(k_cache, v_cache, page_size: int, page_table, table_stride: int,
         row r's page j is pool page r * (slots / page_size) + j;
       - a token index that is negative, at or past table_len * page_size, or
         whose page lies outside the cache is written as zeros and sets
-        STATUS_BAD_INDEX; so does a count outside [0, slots], clamped there.
+        STATUS_BAD_INDEX; so does a count outside [0, min(slots,
+        idx_stride)] (a list never outgrows its row), clamped there.
 
     k_cache, v_cache: [n_pages, page_size, kv_dim] uint16 (bf16 bits).
     Returns (k_out, v_out [rows, slots, kv_dim] uint16, table [rows,
@@ -415,9 +416,10 @@ def gather_kv(k_cache, v_cache, page_size: int, page_table, table_stride: int,
         for j in range(ppr):
             table[r, j] = r * ppr + j
         c = int(counts[r])
-        if c < 0 or c > slots:
+        cmax = min(slots, idx_stride)
+        if c < 0 or c > cmax:
             status |= STATUS_BAD_INDEX
-            c = min(max(c, 0), slots)
+            c = min(max(c, 0), cmax)
         for i in range(c):
             t = int(idx[r * idx_stride + i])
             lp = t // page_size if t >= 0 else -1

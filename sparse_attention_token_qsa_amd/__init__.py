@@ -14,12 +14,14 @@ import torch
 
 from . import _lib
 from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,  # noqa: F401
-                   STATUS_BAD_POSITION, STATUS_NONFINITE_SCORE, QsaError, abi_version, load,
+                   STATUS_BAD_INDEX, STATUS_BAD_POSITION, STATUS_NONFINITE_SCORE, QsaError,
+                   abi_version, load,
                    strerror)
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
+           "qsa_gather_kv",
            "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
@@ -263,6 +265,37 @@ def qsa_score_select_mask(qhat: torch.Tensor, pos: torch.Tensor, pooled: torch.T
     _check(lib.qsa_score_select_mask(_ptr(qhat), _ptr(pos), rows, _ptr(pooled), tokens, budget, _ptr(mask),
                                      _ptr(dev_status), _ptr(workspace), ws_bytes, _stream_ptr(stream)),
            "qsa_score_select_mask")
+
+
+def qsa_gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                  table_stride: int, table_len: int, idx: torch.Tensor, counts: torch.Tensor,
+                  k_out: torch.Tensor, v_out: torch.Tensor, out_table: torch.Tensor,
+                  dev_status: torch.Tensor, stream=None) -> None:
+    """Selected tokens' K/V from a paged cache into contiguous scratch plus the
+    identity page table.  k_cache, v_cache: [n_pages, page_size, kv_dim] bf16;
+    idx: [rows, idx_stride] int32 lists with counts [rows]; k_out, v_out:
+    [rows, slots, kv_dim] bf16; out_table: [rows, slots / page_size] int32."""
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_out, "k_out"), (v_out, "v_out")):
+        _dev(t, name, _BF16_LIKE)
+        _need(t.dim() == 3 and t.is_contiguous(), f"{name} must be a contiguous 3-D tensor")
+    for t, name in ((page_table, "page_table"), (idx, "idx"), (counts, "counts"), (out_table, "out_table"),
+                    (dev_status, "dev_status")):
+        _dev(t, name, (torch.int32,))
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    n_pages, page_size, kv_dim = k_cache.shape
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "v_cache must match k_cache")
+    rows, slots, kd = k_out.shape
+    _need(kd == kv_dim and tuple(v_out.shape) == tuple(k_out.shape), "k_out/v_out must be [rows, slots, kv_dim]")
+    _need(idx.dim() == 2 and idx.shape[0] == rows, "idx must be [rows, idx_stride]")
+    _need(counts.numel() >= rows, "counts needs one entry per row")
+    _need(out_table.numel() >= rows * (slots // max(page_size, 1)), "out_table too small")
+    need = table_len if table_stride == 0 else rows * table_stride
+    _need(page_table.numel() >= need, "page_table too small")
+    lib = load()
+    _check(lib.qsa_gather_kv(_ptr(k_cache), _ptr(v_cache), n_pages, page_size, kv_dim, _ptr(page_table),
+                             table_stride, table_len, _ptr(idx), idx.shape[1], _ptr(counts), rows, slots,
+                             _ptr(k_out), _ptr(v_out), _ptr(out_table), _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_gather_kv")
 
 
 def qsa_rope_inv_freq(rotary_dim: int, rope_theta: float) -> list:

@@ -23,6 +23,7 @@ QSA_ERR_PARAM = -6
 QSA_ERR_LAUNCH = -7
 STATUS_BAD_POSITION = 1
 STATUS_NONFINITE_SCORE = 2
+STATUS_BAD_INDEX = 4
 HEADS = 4
 HEAD_DIM = 128
 RATIO = 4
@@ -33,8 +34,8 @@ MAX_TOKENS = 262147
 EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
-           "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
-ABI_VERSION = 5
+           "qsa_gather_kv", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
+ABI_VERSION = 6
 
 _lib = None
 
@@ -75,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_score_select_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_score_select_mask.argtypes = [P, P, I64, P, I64, I64, P, P, P, I64, P]
     lib.qsa_score_select_mask.restype = ctypes.c_int
+    lib.qsa_gather_kv.argtypes = [P, P, I64, ctypes.c_int32, ctypes.c_int32, P, I64, I64, P, I64, P, I64,
+                                  I64, P, P, P, P, P]
+    lib.qsa_gather_kv.restype = ctypes.c_int
     lib.qsa_rope_inv_freq.argtypes = [I32, F, P]
     lib.qsa_rope_inv_freq.restype = ctypes.c_int
     lib.qsa_strerror.argtypes = [ctypes.c_int]

@@ -256,4 +256,34 @@ int qsa_score_select_mask(const uint16_t* qhat, const int32_t* pos, int64_t rows
                                                 workspace, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_pages,
+                  int32_t page_size, int32_t kv_dim, const int32_t* page_table,
+                  int64_t table_stride, int64_t table_len, const int32_t* idx,
+                  int64_t idx_stride, const int32_t* counts, int64_t rows, int64_t slots,
+                  uint16_t* k_out, uint16_t* v_out, int32_t* out_table, int32_t* dev_status,
+                  void* stream) {
+  if (n_pages < 0 || table_len < 0 || table_stride < 0 || idx_stride < 0 || rows < 0 || slots < 0)
+    return QSA_ERR_EXTENT;
+  if (page_size < 1 || kv_dim < 1 || slots % page_size != 0) return QSA_ERR_PARAM;
+  if (table_stride != 0 && table_stride < table_len) return QSA_ERR_STRIDE;
+  int64_t need, span;
+  if (mul_overflows(rows, slots, &need) || mul_overflows(need, kv_dim, &span) || need / 4 > INT32_MAX)
+    return QSA_ERR_CAPACITY;
+  if (mul_overflows(n_pages, page_size, &need) || mul_overflows(need, kv_dim, &span))
+    return QSA_ERR_CAPACITY;
+  if (mul_overflows(rows, idx_stride, &need) || mul_overflows(rows, table_stride, &need))
+    return QSA_ERR_CAPACITY;
+  if (rows == 0 || slots == 0) return QSA_OK;
+  if (k_out == nullptr || v_out == nullptr || out_table == nullptr || counts == nullptr ||
+      dev_status == nullptr)
+    return QSA_ERR_NULL;
+  if (idx_stride > 0 && idx == nullptr) return QSA_ERR_NULL;
+  if (table_len > 0 && page_table == nullptr) return QSA_ERR_NULL;
+  if (n_pages > 0 && (k_cache == nullptr || v_cache == nullptr)) return QSA_ERR_NULL;
+  return launch_status(qsa::launch_gather_kv(k_cache, v_cache, n_pages, page_size, kv_dim, page_table,
+                                             table_stride, table_len, idx, idx_stride, counts, rows, slots,
+                                             k_out, v_out, out_table, dev_status,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

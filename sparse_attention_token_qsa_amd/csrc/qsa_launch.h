@@ -84,6 +84,13 @@ struct RingJob {
 int64_t ring_splits(int64_t rows, int64_t cols, int64_t target);
 hipError_t launch_ring(const RingJob& j, int64_t target, hipStream_t stream);
 
+// Decode K/V gather from a paged cache (gather.hip).
+hipError_t launch_gather_kv(const uint16_t* k, const uint16_t* v, int64_t n_pages, int page_size,
+                            int kv_dim, const int32_t* table, int64_t table_stride, int64_t table_len,
+                            const int32_t* idx, int64_t idx_stride, const int32_t* counts, int64_t rows,
+                            int64_t slots, uint16_t* ko, uint16_t* vo, int32_t* otable, int32_t* status,
+                            hipStream_t stream);
+
 // Fused score -> select for prefill batches (fused.hip).
 int64_t score_select_workspace_bytes(int64_t rows, int64_t tokens, int keep_max);
 hipError_t launch_score_select(const uint16_t* qhat, const int32_t* pos, int64_t rows,

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 5
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 6
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -257,6 +257,32 @@ def test_score_select_refusals(lib):
     need = lib.qsa_score_select_workspace_bytes(8, 4096, 2048)
     assert fused(lib, ws_bytes=need - 1) == CAP
     assert fused(lib, ws=0x100000 + 16, ws_bytes=need) == PARAM
+
+
+def gather(lib, **kw):
+    a = dict(k=P, v=P, n_pages=64, page_size=16, kv_dim=512, table=P, table_stride=0, table_len=64,
+             idx=P, idx_stride=2051, counts=P, rows=4, slots=2064, ko=P, vo=P, otab=P, status=P)
+    a.update(kw)
+    return lib.qsa_gather_kv(a["k"], a["v"], a["n_pages"], a["page_size"], a["kv_dim"], a["table"],
+                             a["table_stride"], a["table_len"], a["idx"], a["idx_stride"], a["counts"],
+                             a["rows"], a["slots"], a["ko"], a["vo"], a["otab"], a["status"], None)
+
+
+def test_gather_kv_refusals(lib):
+    assert gather(lib, rows=0) == OK
+    assert gather(lib, slots=0) == OK
+    assert gather(lib, rows=0, k=None, v=None, ko=None, vo=None, otab=None, status=None) == OK
+    for k in ("k", "v", "table", "idx", "counts", "ko", "vo", "otab", "status"):
+        assert gather(lib, **{k: None}) == NULL, k
+    for k in ("n_pages", "table_len", "table_stride", "idx_stride", "rows", "slots"):
+        assert gather(lib, **{k: -1}) == EXTENT, k
+    assert gather(lib, page_size=0) == PARAM
+    assert gather(lib, kv_dim=0) == PARAM
+    assert gather(lib, slots=2051) == PARAM
+    assert gather(lib, table_stride=63) == STRIDE
+    assert gather(lib, rows=2**40, slots=2**20) == CAP
+    assert gather(lib, n_pages=2**50) == CAP
+    assert gather(lib, rows=2**33, slots=16) == CAP
 
 
 def prep(lib, **kw):

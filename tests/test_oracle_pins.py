@@ -644,3 +644,7 @@ def test_gather_bad_indices_and_counts_write_zeros_and_flag():
                                    np.array([bad_count]), 1, 8)
         assert st == O.STATUS_BAD_INDEX
         assert np.all(ko[0, :8 if bad_count > 0 else 0] == 7) and not ko[0, 8:].any()
+    # a list row shorter than the scratch bounds the count too
+    ko, _, _, st = O.gather_kv(kc, vc, page_size, table, 0, 3, np.zeros((1, 6), np.int32), 6,
+                               np.array([7]), 1, 8)
+    assert st == O.STATUS_BAD_INDEX and np.all(ko[0, :6] == 7) and not ko[0, 6:].any()
