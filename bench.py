@@ -394,6 +394,90 @@ def cpu_baseline(w, budget_s: float):
 
 # ----------------------------------------------------------------------------
 
+def launch_us(fn, torch, reps: int = 20):
+    """Per-launch microseconds of `fn` launched `reps` times back to back
+    between one pair of HIP events, queued behind a busy GPU."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    prime(torch)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1e3 / reps, 3)
+
+
+KV_DIM = 512     # synthetic attention K/V vector: 2 KV heads x head dim 256, bf16
+PAGE_SIZE = 16   # tokens per cache page
+
+
+def decode_next(d: Device, torch, qsa):
+    """The decode consumers of the selection on one workload: the index-list
+    selector and the K/V gather from a paged cache (seeded random K/V, pages
+    in a random order) into contiguous scratch."""
+    w = d.w
+    budget = w["budget"]
+    stride = budget + 3
+    slots = -(-stride // PAGE_SIZE) * PAGE_SIZE
+    idx = torch.empty((d.rows, stride), dtype=torch.int32, device="cuda:0")
+    counts = torch.empty(d.rows, dtype=torch.int32, device="cuda:0")
+    d.pool()
+    d.prep()
+    d.score()
+    sel_us = launch_us(lambda: qsa.qsa_select_indices(d.scores, d.cols, d.pos, d.T, budget, idx, counts,
+                                                      d.status), torch)
+    n_pages = -(-d.T // PAGE_SIZE)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(1000 + int(w.get("wid", 0)))
+    kc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE_SIZE, KV_DIM), dtype=torch.int16, device="cuda:0",
+                       generator=g)
+    vc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE_SIZE, KV_DIM), dtype=torch.int16, device="cuda:0",
+                       generator=g)
+    table = torch.randperm(n_pages, device="cuda:0", generator=g).to(torch.int32)
+    ko = torch.empty((d.rows, slots, KV_DIM), dtype=torch.int16, device="cuda:0")
+    vo = torch.empty_like(ko)
+    otab = torch.empty((d.rows, slots // PAGE_SIZE), dtype=torch.int32, device="cuda:0")
+    g_us = launch_us(lambda: qsa.qsa_gather_kv(kc, vc, table, 0, n_pages, idx, counts, ko, vo, otab, d.status),
+                     torch)
+    if qsa.check_status(d.status) != 0:
+        raise RuntimeError("device status set in the decode gather")
+    n_sel = int(counts.sum().item())
+    alg = 4 * KV_DIM * n_sel + 4 * KV_DIM * d.rows * slots + 4 * d.rows * (stride + 1 + slots // PAGE_SIZE)
+    gbs = alg / (g_us * 1e-6) / 1e9
+    del kc, vc, ko, vo
+    return {"select_indices_us": sel_us,
+            "kv_gather": {"us": g_us, "kv_dim": KV_DIM, "page_size": PAGE_SIZE, "slots": slots,
+                          "entries": n_sel, "alg_bytes": alg, "achieved_GBs": round(gbs, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def fused_prefill(d: Device, torch, qsa):
+    """qsa_score_select_mask (score -> select without the score matrix) on
+    the main workload, beside the two-call path it replaces; masks compared."""
+    budget = d.w["budget"]
+    n = qsa.qsa_score_select_workspace_bytes(d.rows, d.T, budget)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    mask = torch.empty_like(d.mask)
+    d.pool()
+    d.prep()
+    fused_us = launch_us(lambda: qsa.qsa_score_select_mask(d.qhat, d.pos, d.pooled, d.T, budget, mask, d.status,
+                                                           ws), torch, reps=10)
+
+    def two():
+        d.score()
+        d.select()
+    sep_us = launch_us(two, torch, reps=10)
+    same = bool(torch.equal(mask, d.mask))
+    del ws, mask
+    torch.cuda.empty_cache()
+    return {"fused_us": fused_us, "score_then_select_us": sep_us, "masks_equal": same,
+            "workspace_bytes": n}
+
+
 def side_figures(torch, qsa, synth):
     """select+mask us/row on the 64k/256k decode workloads and the one-row
     64k/256k shapes: per-kernel event means over 20 launches after 5 warm-ups
@@ -422,6 +506,7 @@ def side_figures(torch, qsa, synth):
                     "pairs_per_s": round(d.pairs / (sum(b2b.values()) * 1e-6), 1),
                     "kernels_back_to_back_us": b2b,
                     "kernels": rep}
+        out[key].update(decode_next(d, torch, qsa))
         del d
         torch.cuda.empty_cache()
     return out
@@ -472,6 +557,7 @@ def main():
     roof["traffic"] = traffic_for(dom, w["name"])
 
     side = {} if args.no_side else side_figures(torch, qsa, synth)
+    fused = None if args.no_side else fused_prefill(d, torch, qsa)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
 
     line = {
@@ -500,6 +586,7 @@ def main():
         "kernels": rep,
         "roofline": roof,
         "side_workloads": side,
+        "fused_score_select": fused,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
