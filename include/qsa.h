@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 6
+#define QSA_ABI_VERSION 7
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -58,6 +58,7 @@ extern "C" {
 #define QSA_STATUS_BAD_POSITION 1   /* pos[r] outside [0, tokens) */
 #define QSA_STATUS_NONFINITE_SCORE 2 /* a NaN or +-Inf among a row's visible block scores */
 #define QSA_STATUS_BAD_INDEX 4       /* qsa_gather_kv: a token outside the cache, or a bad count */
+#define QSA_STATUS_BAD_GEOMETRY 8    /* *_dev calls: the device token count outside [0, max_tokens] */
 
 /*
  * qsa_pool_keys -- pooled key of every 4-token block in
@@ -329,6 +330,48 @@ int qsa_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_pa
                   int64_t idx_stride, const int32_t* counts, int64_t rows, int64_t slots,
                   uint16_t* k_out, uint16_t* v_out, int32_t* out_table, int32_t* dev_status,
                   void* stream);
+
+/*
+ * Device-geometry calls, for a decode step captured once as a HIP graph and
+ * replayed while the cache grows.  A graph freezes every host argument it was
+ * captured with; these calls take the live cache length from a device int32
+ * (*dev_tokens, 0 <= T <= max_tokens) read when the kernels run, and size their
+ * launches for max_tokens, the ceiling.  Positions (pos) are already device
+ * data.  A T outside [0, max_tokens] is clamped into it and sets
+ * QSA_STATUS_BAD_GEOMETRY.  Refusals are those of the host-count call with
+ * tokens = max_tokens, plus QSA_ERR_NULL for a NULL dev_tokens.
+ *
+ * qsa_pool_window -- [QSA] pool_new_blocks: a decode step pools only the
+ * blocks its new tokens completed.  Pools the last n_blocks complete blocks,
+ * [max(0, T/4 - n_blocks), T/4), with qsa_pool_keys' arithmetic; pooling a
+ * block again writes the same bytes, so n_blocks only has to cover the
+ * blocks completed since the previous call (1 for one-token decode steps).
+ * n_blocks <= max_tokens / 4 (QSA_ERR_EXTENT); 0 enqueues nothing.
+ */
+int qsa_pool_window(const uint16_t* raw_keys, int64_t key_stride, int64_t max_tokens,
+                    const uint16_t* k_norm_w, int32_t rotary_dim, float rope_theta, float rms_eps,
+                    const int32_t* dev_tokens, int64_t n_blocks, uint16_t* pooled,
+                    int32_t* dev_status, void* stream);
+
+/* qsa_prep_queries with the live cache length on the device (validity of pos). */
+int qsa_prep_queries_dev(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                         const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
+                         float rms_eps, const int32_t* dev_tokens, int64_t max_tokens,
+                         uint16_t* qhat, int32_t* dev_status, void* stream);
+
+/* qsa_score_prepped with the live cache length on the device; score_cols >=
+ * max_tokens / 4.  Workgroups past a batch's longest visible prefix exit. */
+int qsa_score_prepped_dev(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                          const uint16_t* pooled, const int32_t* dev_tokens, int64_t max_tokens,
+                          float* scores, int64_t score_cols, int64_t scores_len,
+                          int32_t* dev_status, void* stream);
+
+/* qsa_select_indices with the live cache length on the device; the index
+ * lists do not depend on the cache length beyond the validity of pos. */
+int qsa_select_indices_dev(const float* scores, int64_t score_cols, int64_t scores_len,
+                           const int32_t* pos, int64_t rows, const int32_t* dev_tokens,
+                           int64_t max_tokens, int64_t budget, int32_t* idx, int64_t idx_stride,
+                           int32_t* counts, int32_t* dev_status, void* stream);
 
 /*
  * qsa_rope_inv_freq -- host only: the rotary frequencies the kernels use,

@@ -14,14 +14,16 @@ import torch
 
 from . import _lib
 from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,  # noqa: F401
-                   STATUS_BAD_INDEX, STATUS_BAD_POSITION, STATUS_NONFINITE_SCORE, QsaError,
+                   STATUS_BAD_GEOMETRY, STATUS_BAD_INDEX, STATUS_BAD_POSITION,
+                   STATUS_NONFINITE_SCORE, QsaError,
                    abi_version, load,
                    strerror)
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
-           "qsa_gather_kv",
+           "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
+           "qsa_select_indices_dev",
            "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
@@ -296,6 +298,98 @@ def qsa_gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torc
                              table_stride, table_len, _ptr(idx), idx.shape[1], _ptr(counts), rows, slots,
                              _ptr(k_out), _ptr(v_out), _ptr(out_table), _ptr(dev_status), _stream_ptr(stream)),
            "qsa_gather_kv")
+
+
+def _dev_tokens(dev_tokens: torch.Tensor) -> None:
+    _dev(dev_tokens, "dev_tokens", (torch.int32,))
+    _need(dev_tokens.numel() >= 1, "dev_tokens needs one int32")
+
+
+def qsa_pool_window(raw_keys: torch.Tensor, k_norm_w: torch.Tensor, rotary_dim: int,
+                    rope_theta: float, rms_eps: float, dev_tokens: torch.Tensor, n_blocks: int,
+                    pooled: torch.Tensor, dev_status: torch.Tensor, stream=None) -> None:
+    """Pool the last n_blocks complete blocks of a cache of dev_tokens[0] tokens;
+    raw_keys [max_tokens, >=128] bf16 (its rows are the ceiling)."""
+    _dev(raw_keys, "raw_keys", _BF16_LIKE)
+    _dev(k_norm_w, "k_norm_w", _BF16_LIKE)
+    _dev(pooled, "pooled", _BF16_LIKE)
+    _dev(dev_status, "dev_status", (torch.int32,))
+    _dev_tokens(dev_tokens)
+    key_stride = _rows_2d(raw_keys, "raw_keys", HEAD_DIM)
+    max_tokens = raw_keys.shape[0]
+    _need(k_norm_w.numel() == HEAD_DIM and k_norm_w.is_contiguous(), "k_norm_w must hold 128 values")
+    _need(pooled.is_contiguous() and pooled.dim() == 2 and pooled.shape[1] == HEAD_DIM
+          and pooled.shape[0] >= max_tokens // RATIO, "pooled must be contiguous [max_tokens/4, 128]")
+    lib = load()
+    _check(lib.qsa_pool_window(_ptr(raw_keys), key_stride, max_tokens, _ptr(k_norm_w), rotary_dim, rope_theta,
+                               rms_eps, _ptr(dev_tokens), n_blocks, _ptr(pooled), _ptr(dev_status),
+                               _stream_ptr(stream)), "qsa_pool_window")
+
+
+def qsa_prep_queries_dev(q: torch.Tensor, pos: torch.Tensor, q_norm_w: torch.Tensor, rotary_dim: int,
+                         rope_theta: float, rms_eps: float, dev_tokens: torch.Tensor, max_tokens: int,
+                         qhat: torch.Tensor, dev_status: torch.Tensor, stream=None) -> None:
+    """qsa_prep_queries with the live cache length in dev_tokens[0]."""
+    _dev(q, "q", _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(q_norm_w, "q_norm_w", _BF16_LIKE)
+    _dev(qhat, "qhat", _BF16_LIKE)
+    _dev(dev_status, "dev_status", (torch.int32,))
+    _dev_tokens(dev_tokens)
+    q_stride = _rows_2d(q, "q", HEADS * HEAD_DIM)
+    rows = q.shape[0]
+    _need(pos.is_contiguous() and pos.numel() == rows, "pos must be contiguous [rows]")
+    _need(q_norm_w.numel() == HEAD_DIM and q_norm_w.is_contiguous(), "q_norm_w must hold 128 values")
+    _need(qhat.is_contiguous() and qhat.numel() >= rows * HEADS * HEAD_DIM,
+          "qhat must be contiguous [rows, 4, 128]")
+    lib = load()
+    _check(lib.qsa_prep_queries_dev(_ptr(q), q_stride, _ptr(pos), rows, _ptr(q_norm_w), rotary_dim, rope_theta,
+                                    rms_eps, _ptr(dev_tokens), max_tokens, _ptr(qhat), _ptr(dev_status),
+                                    _stream_ptr(stream)), "qsa_prep_queries_dev")
+
+
+def qsa_score_prepped_dev(qhat: torch.Tensor, pos: torch.Tensor, pooled: torch.Tensor,
+                          dev_tokens: torch.Tensor, max_tokens: int, scores: torch.Tensor, score_cols: int,
+                          dev_status: torch.Tensor, stream=None) -> None:
+    """qsa_score_prepped with the live cache length in dev_tokens[0]."""
+    _dev(qhat, "qhat", _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(pooled, "pooled", _BF16_LIKE)
+    _dev(scores, "scores", (torch.float32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    _dev_tokens(dev_tokens)
+    rows = pos.numel()
+    _need(pos.is_contiguous(), "pos must be contiguous")
+    _need(qhat.is_contiguous() and qhat.numel() >= rows * HEADS * HEAD_DIM,
+          "qhat must be contiguous [rows, 4, 128]")
+    _need(pooled.is_contiguous() and pooled.numel() >= (max_tokens // RATIO) * HEAD_DIM,
+          "pooled must hold [max_tokens/4, 128]")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    lib = load()
+    _check(lib.qsa_score_prepped_dev(_ptr(qhat), _ptr(pos), rows, _ptr(pooled), _ptr(dev_tokens), max_tokens,
+                                     _ptr(scores), score_cols, scores.numel(), _ptr(dev_status),
+                                     _stream_ptr(stream)), "qsa_score_prepped_dev")
+
+
+def qsa_select_indices_dev(scores: torch.Tensor, score_cols: int, pos: torch.Tensor,
+                           dev_tokens: torch.Tensor, max_tokens: int, budget: int, idx: torch.Tensor,
+                           counts: torch.Tensor, dev_status: torch.Tensor, stream=None) -> None:
+    """qsa_select_indices with the live cache length in dev_tokens[0]."""
+    _dev(scores, "scores", (torch.float32,))
+    _dev(pos, "pos", (torch.int32,))
+    _dev(idx, "idx", (torch.int32,))
+    _dev(counts, "counts", (torch.int32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    _dev_tokens(dev_tokens)
+    rows = pos.numel()
+    _need(pos.is_contiguous() and scores.is_contiguous(), "pos and scores must be contiguous")
+    idx_stride = _rows_2d(idx, "idx", budget + RATIO - 1)
+    _need(idx.shape[0] >= rows, "idx needs a row per position")
+    _need(counts.is_contiguous() and counts.numel() >= rows, "counts must be contiguous [rows]")
+    lib = load()
+    _check(lib.qsa_select_indices_dev(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, _ptr(dev_tokens),
+                                      max_tokens, budget, _ptr(idx), idx_stride, _ptr(counts), _ptr(dev_status),
+                                      _stream_ptr(stream)), "qsa_select_indices_dev")
 
 
 def qsa_rope_inv_freq(rotary_dim: int, rope_theta: float) -> list:

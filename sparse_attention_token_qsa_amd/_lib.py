@@ -24,6 +24,7 @@ QSA_ERR_LAUNCH = -7
 STATUS_BAD_POSITION = 1
 STATUS_NONFINITE_SCORE = 2
 STATUS_BAD_INDEX = 4
+STATUS_BAD_GEOMETRY = 8
 HEADS = 4
 HEAD_DIM = 128
 RATIO = 4
@@ -34,8 +35,9 @@ MAX_TOKENS = 262147
 EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
-           "qsa_gather_kv", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
-ABI_VERSION = 6
+           "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
+           "qsa_select_indices_dev", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
+ABI_VERSION = 7
 
 _lib = None
 
@@ -79,6 +81,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_gather_kv.argtypes = [P, P, I64, ctypes.c_int32, ctypes.c_int32, P, I64, I64, P, I64, P, I64,
                                   I64, P, P, P, P, P]
     lib.qsa_gather_kv.restype = ctypes.c_int
+    F32 = ctypes.c_float
+    I32 = ctypes.c_int32
+    lib.qsa_pool_window.argtypes = [P, I64, I64, P, I32, F32, F32, P, I64, P, P, P]
+    lib.qsa_pool_window.restype = ctypes.c_int
+    lib.qsa_prep_queries_dev.argtypes = [P, I64, P, I64, P, I32, F32, F32, P, I64, P, P, P]
+    lib.qsa_prep_queries_dev.restype = ctypes.c_int
+    lib.qsa_score_prepped_dev.argtypes = [P, P, I64, P, P, I64, P, I64, I64, P, P]
+    lib.qsa_score_prepped_dev.restype = ctypes.c_int
+    lib.qsa_select_indices_dev.argtypes = [P, I64, I64, P, I64, P, I64, I64, P, I64, P, P, P]
+    lib.qsa_select_indices_dev.restype = ctypes.c_int
     lib.qsa_rope_inv_freq.argtypes = [I32, F, P]
     lib.qsa_rope_inv_freq.restype = ctypes.c_int
     lib.qsa_strerror.argtypes = [ctypes.c_int]

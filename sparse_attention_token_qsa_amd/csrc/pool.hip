@@ -31,6 +31,11 @@ struct PoolArgs {
   int64_t first_block;
   int64_t n_blocks;
   RopeParams rp;
+  // window mode (dev_tokens set): the last n_blocks complete blocks of a
+  // cache of *dev_tokens tokens (at most `ceiling`), first_block unused
+  const int32_t* dev_tokens;
+  int64_t ceiling;
+  int32_t* status;
 };
 
 __device__ __forceinline__ void unpack8(const uint4 u, float (&v)[8]) {
@@ -77,8 +82,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
   const int g = tid & 15;     // channel group: channels 8g .. 8g+7
   const int64_t group_first = static_cast<int64_t>(blockIdx.x) * kPoolBlocksPerGroup;
   const int64_t blk = group_first + slot;
-  const bool live = blk < a.n_blocks;
-  const int64_t b = a.first_block + blk;
+  int64_t first = a.first_block, count = a.n_blocks;
+  if (a.dev_tokens != nullptr) {
+    const int64_t complete = live_tokens(a.ceiling, a.dev_tokens, a.status) / kRatio;
+    first = complete > a.n_blocks ? complete - a.n_blocks : 0;
+    count = complete - first;
+  }
+  const bool live = blk < count;
+  const int64_t b = first + blk;
 
   // raw keys first: four 16-byte token rows per lane
   uint4 v[4];
@@ -211,8 +222,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
 
 hipError_t launch_pool(const uint16_t* raw, int64_t key_stride, const uint16_t* w,
                        const RopeParams& rp, int64_t first_block, int64_t n_blocks,
-                       uint16_t* pooled, hipStream_t stream) {
-  PoolArgs a{raw, key_stride, w, pooled, first_block, n_blocks, rp};
+                       uint16_t* pooled, hipStream_t stream, const int32_t* dev_tokens,
+                       int64_t ceiling, int32_t* status) {
+  PoolArgs a{raw, key_stride, w, pooled, first_block, n_blocks, rp, dev_tokens, ceiling, status};
   const int64_t groups = (n_blocks + kPoolBlocksPerGroup - 1) / kPoolBlocksPerGroup;
   if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool vec = (key_stride % 8 == 0) && (reinterpret_cast<uintptr_t>(raw) % 16 == 0) &&

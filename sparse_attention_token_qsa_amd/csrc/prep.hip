@@ -27,7 +27,8 @@ struct PrepArgs {
   const int32_t* pos;
   int64_t rows;
   const uint16_t* w;
-  int64_t tokens;
+  int64_t tokens;             // the ceiling when dev_tokens is set
+  const int32_t* dev_tokens;  // optional live cache length on the device
   uint16_t* qhat;
   int32_t* status;
   int q_vec;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) {
     int p = 0, ok = 0;
     if (rr < a.rows) {
       p = a.pos[rr];
-      ok = p >= 0 && p < a.tokens;
+      ok = p >= 0 && p < live_tokens(a.tokens, a.dev_tokens, a.status);
       if (!ok) atomicOr(a.status, 1);
     }
     ppos[tid] = p;
@@ -187,8 +188,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) {
 
 hipError_t launch_prep(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
                        const uint16_t* w, const RopeParams& rp, int64_t tokens, uint16_t* qhat,
-                       int32_t* status, hipStream_t stream) {
+                       int32_t* status, hipStream_t stream, const int32_t* dev_tokens) {
   PrepArgs a{};
+  a.dev_tokens = dev_tokens;
   a.q = q;
   a.q_stride = q_stride;
   a.pos = pos;

@@ -286,4 +286,93 @@ int qsa_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_pa
                                              static_cast<hipStream_t>(stream)));
 }
 
+int qsa_pool_window(const uint16_t* raw_keys, int64_t key_stride, int64_t max_tokens,
+                    const uint16_t* k_norm_w, int32_t rotary_dim, float rope_theta, float rms_eps,
+                    const int32_t* dev_tokens, int64_t n_blocks, uint16_t* pooled,
+                    int32_t* dev_status, void* stream) {
+  if (max_tokens < 0 || n_blocks < 0) return QSA_ERR_EXTENT;
+  if (n_blocks > max_tokens / QSA_RATIO) return QSA_ERR_EXTENT;
+  if (key_stride < QSA_HEAD_DIM) return QSA_ERR_STRIDE;
+  const int rc = check_rope(rotary_dim, rope_theta, rms_eps);
+  if (rc != QSA_OK) return rc;
+  if (max_tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (n_blocks == 0) return QSA_OK;
+  if (raw_keys == nullptr || k_norm_w == nullptr || pooled == nullptr || dev_tokens == nullptr ||
+      dev_status == nullptr)
+    return QSA_ERR_NULL;
+  int64_t span;
+  if (mul_overflows(max_tokens, key_stride, &span)) return QSA_ERR_CAPACITY;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_pool(raw_keys, key_stride, k_norm_w, rp, 0, n_blocks, pooled,
+                                        static_cast<hipStream_t>(stream), dev_tokens, max_tokens,
+                                        dev_status));
+}
+
+int qsa_prep_queries_dev(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                         const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
+                         float rms_eps, const int32_t* dev_tokens, int64_t max_tokens,
+                         uint16_t* qhat, int32_t* dev_status, void* stream) {
+  if (rows < 0 || max_tokens < 0) return QSA_ERR_EXTENT;
+  if (q_stride < QSA_HEADS * QSA_HEAD_DIM) return QSA_ERR_STRIDE;
+  const int rc = check_rope(rotary_dim, rope_theta, rms_eps);
+  if (rc != QSA_OK) return rc;
+  if (max_tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0) return QSA_OK;
+  if (q == nullptr || pos == nullptr || q_norm_w == nullptr || qhat == nullptr ||
+      dev_status == nullptr || dev_tokens == nullptr)
+    return QSA_ERR_NULL;
+  int64_t need;
+  if (mul_overflows(rows, q_stride, &need)) return QSA_ERR_CAPACITY;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_prep(q, q_stride, pos, rows, q_norm_w, rp, max_tokens, qhat, dev_status,
+                                        static_cast<hipStream_t>(stream), dev_tokens));
+}
+
+int qsa_score_prepped_dev(const uint16_t* qhat, const int32_t* pos, int64_t rows,
+                          const uint16_t* pooled, const int32_t* dev_tokens, int64_t max_tokens,
+                          float* scores, int64_t score_cols, int64_t scores_len,
+                          int32_t* dev_status, void* stream) {
+  if (rows < 0 || max_tokens < 0 || score_cols < 0 || scores_len < 0) return QSA_ERR_EXTENT;
+  if (score_cols < max_tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  if (max_tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0 || max_tokens == 0) return QSA_OK;
+  if (qhat == nullptr || pos == nullptr || dev_status == nullptr || dev_tokens == nullptr) return QSA_ERR_NULL;
+  if (max_tokens >= QSA_RATIO && (pooled == nullptr || scores == nullptr)) return QSA_ERR_NULL;
+  return launch_status(qsa::launch_score_prepped(qhat, pos, rows, pooled, max_tokens, scores, score_cols,
+                                                 dev_status, static_cast<hipStream_t>(stream), dev_tokens));
+}
+
+int qsa_select_indices_dev(const float* scores, int64_t score_cols, int64_t scores_len,
+                           const int32_t* pos, int64_t rows, const int32_t* dev_tokens,
+                           int64_t max_tokens, int64_t budget, int32_t* idx, int64_t idx_stride,
+                           int32_t* counts, int32_t* dev_status, void* stream) {
+  if (dev_tokens == nullptr && rows > 0 && max_tokens > 0) return QSA_ERR_NULL;
+  if (rows < 0 || max_tokens < 0 || score_cols < 0 || scores_len < 0 || idx_stride < 0) return QSA_ERR_EXTENT;
+  if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
+    return QSA_ERR_BUDGET;
+  if (score_cols < max_tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  if (idx_stride < budget + QSA_RATIO - 1) return QSA_ERR_STRIDE;
+  if (max_tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
+  if (mul_overflows(rows, idx_stride, &need)) return QSA_ERR_CAPACITY;
+  if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  if (rows == 0 || max_tokens == 0) return QSA_OK;
+  if (pos == nullptr || idx == nullptr || counts == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
+  if (max_tokens >= QSA_RATIO && scores == nullptr) return QSA_ERR_NULL;
+  return launch_status(qsa::launch_select_indices(scores, score_cols, pos, rows, max_tokens,
+                                                  static_cast<int>(budget / QSA_RATIO), idx, idx_stride, counts,
+                                                  dev_status, static_cast<hipStream_t>(stream), dev_tokens));
+}
+
 }  // extern "C"

@@ -11,6 +11,18 @@ constexpr int kHeadDim = 128;
 constexpr int kRatio = 4;
 constexpr int kMaxKeep = 512;
 constexpr int kMaxHalfRotary = 64;
+// The live cache length of a launch: the device word when one is given (read
+// by every thread; a value outside [0, ceiling] is clamped and sets status bit
+// 8 once per launch), else the host count.  Device words let one captured
+// graph serve a cache that grows between replays.
+__device__ __forceinline__ int64_t live_tokens(int64_t ceiling, const int32_t* dev, int32_t* status) {
+  if (dev == nullptr) return ceiling;
+  const int64_t t = *dev;
+  if (t >= 0 && t <= ceiling) return t;
+  if (status != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, 8);
+  return t < 0 ? 0 : ceiling;
+}
+
 // score scale 1/sqrt(head dim), rounded once to f32
 constexpr float kScale = static_cast<float>(0.088388347648318440550);
 

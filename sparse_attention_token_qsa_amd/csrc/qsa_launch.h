@@ -13,22 +13,28 @@ struct RopeParams {
   float inv_freq[64];
 };
 
+// With dev_tokens set: pool the last n_blocks complete blocks of a cache of
+// *dev_tokens tokens (ceiling at most), first_block unused.
 hipError_t launch_pool(const uint16_t* raw, int64_t key_stride, const uint16_t* w,
                        const RopeParams& rp, int64_t first_block, int64_t n_blocks,
-                       uint16_t* pooled, hipStream_t stream);
+                       uint16_t* pooled, hipStream_t stream, const int32_t* dev_tokens = nullptr,
+                       int64_t ceiling = 0, int32_t* status = nullptr);
 
 hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
                         const uint16_t* w, const RopeParams& rp, const uint16_t* pooled,
                         int64_t tokens, float* scores, int64_t score_cols, int32_t* status,
                         hipStream_t stream);
 
+// dev_tokens (optional, below): a device int32 holding the live cache length;
+// `tokens` is then its ceiling (launch geometry and buffer extents).
 hipError_t launch_prep(const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
                        const uint16_t* w, const RopeParams& rp, int64_t tokens, uint16_t* qhat,
-                       int32_t* status, hipStream_t stream);
+                       int32_t* status, hipStream_t stream, const int32_t* dev_tokens = nullptr);
 
 hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
                                 const uint16_t* pooled, int64_t tokens, float* scores,
-                                int64_t score_cols, int32_t* status, hipStream_t stream);
+                                int64_t score_cols, int32_t* status, hipStream_t stream,
+                                const int32_t* dev_tokens = nullptr);
 
 hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t* pos,
                          int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
@@ -38,7 +44,7 @@ hipError_t launch_select(const float* scores, int64_t score_cols, const int32_t*
 hipError_t launch_select_indices(const float* scores, int64_t score_cols, const int32_t* pos,
                                  int64_t rows, int64_t tokens, int keep_max, int32_t* idx,
                                  int64_t idx_stride, int32_t* counts, int32_t* status,
-                                 hipStream_t stream);
+                                 hipStream_t stream, const int32_t* dev_tokens = nullptr);
 
 // Split select for few long rows (select_split.hip): two launches over a
 // caller-provided workspace of select_split_workspace_bytes(rows, tokens).

@@ -52,7 +52,8 @@ struct ScoreArgs {
   int64_t rows;
   const uint16_t* w;
   const uint16_t* pooled;
-  int64_t tokens;
+  int64_t tokens;             // the ceiling when dev_tokens is set
+  const int32_t* dev_tokens;  // optional live cache length on the device
   float* scores;
   int64_t score_cols;
   int32_t* status;
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
       const int64_t r = row0 + lane;
       if (r < a.rows) {
         p = a.pos[r];
-        if (p >= 0 && p < a.tokens)
+        if (p >= 0 && p < live_tokens(a.tokens, a.dev_tokens, a.status))
           n = (p + 1) / kRatio;
         else if (split == 0)
           atomicOr(a.status, 1);
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
     const int lr = (p * 16 + hv_local) >> 2;
     float x[8];
     unpack_bf16x8(xq[p], x);
-    if (!(ppos[lr] >= 0 && ppos[lr] < a.tokens)) {
+    if (!(ppos[lr] >= 0 && ppos[lr] < live_tokens(a.tokens, a.dev_tokens, nullptr))) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.0f;
     }
@@ -504,7 +505,8 @@ struct RingArgs {
   const int32_t* pos;
   int64_t rows;
   const uint16_t* pooled;
-  int64_t tokens;
+  int64_t tokens;             // the ceiling when dev_tokens is set
+  const int32_t* dev_tokens;  // optional live cache length on the device
   int bstride;  // column j scores the pooled key of block j * bstride
   float* scores;
   int64_t score_cols;
@@ -647,7 +649,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
         const int64_t r = row0 + lr;
         if (r < a.rows) {
           const int p = a.pos[r];
-          if (p >= 0 && p < a.tokens)
+          if (p >= 0 && p < live_tokens(a.tokens, a.dev_tokens, a.status))
             n = ((p + 1) / kRatio + a.bstride - 1) / a.bstride;
           else if (split == 0 && a.status != nullptr)
             atomicOr(a.status, 1);
@@ -904,6 +906,7 @@ hipError_t launch_score_ring(const ScoreArgs& s, hipStream_t stream) {
   a.rows = s.rows;
   a.pooled = s.pooled;
   a.tokens = s.tokens;
+  a.dev_tokens = s.dev_tokens;
   a.bstride = 1;
   a.scores = s.scores;
   a.score_cols = s.score_cols;
@@ -1003,8 +1006,10 @@ hipError_t launch_score(const uint16_t* q, int64_t q_stride, const int32_t* pos,
 
 hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
                                 const uint16_t* pooled, int64_t tokens, float* scores,
-                                int64_t score_cols, int32_t* status, hipStream_t stream) {
+                                int64_t score_cols, int32_t* status, hipStream_t stream,
+                                const int32_t* dev_tokens) {
   ScoreArgs a{};
+  a.dev_tokens = dev_tokens;
   a.qhat = qhat;
   a.pos = pos;
   a.rows = rows;

@@ -44,7 +44,8 @@ struct SelectArgs {
   const float* scores;
   int64_t score_cols;
   const int32_t* pos;
-  int64_t tokens;
+  int64_t tokens;             // mask row length; the ceiling when dev_tokens is set
+  const int32_t* dev_tokens;  // optional live cache length on the device
   int keep_max;
   uint8_t* mask;
   int32_t* status;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
     for (int i = tid; i < cap; i += NT) irow[i] = i <= last ? i : -1;
     if (tid == 0) a.counts[row] = static_cast<int32_t>(last + 1);
   };
-  if (p < 0 || p >= T) {
+  if (p < 0 || p >= live_tokens(T, a.dev_tokens, a.status)) {
     if constexpr (IDX)
       write_prefix_idx(-1);
     else
@@ -415,8 +416,9 @@ hipError_t launch_select_flagged(const float* scores, int64_t score_cols, const 
 hipError_t launch_select_indices(const float* scores, int64_t score_cols, const int32_t* pos,
                                  int64_t rows, int64_t tokens, int keep_max, int32_t* idx,
                                  int64_t idx_stride, int32_t* counts, int32_t* status,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const int32_t* dev_tokens) {
   SelectArgs a{};
+  a.dev_tokens = dev_tokens;
   a.scores = scores;
   a.score_cols = score_cols;
   a.pos = pos;

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 6
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 7
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -283,6 +283,37 @@ def test_gather_kv_refusals(lib):
     assert gather(lib, rows=2**40, slots=2**20) == CAP
     assert gather(lib, n_pages=2**50) == CAP
     assert gather(lib, rows=2**33, slots=16) == CAP
+
+
+def pool_window(lib, **kw):
+    a = dict(raw=P, ks=128, mt=4096, w=P, rd=64, th=1e4, eps=1e-6, dt=P, nb=1, out=P, st=P)
+    a.update(kw)
+    return lib.qsa_pool_window(a["raw"], a["ks"], a["mt"], a["w"], a["rd"], a["th"], a["eps"], a["dt"], a["nb"],
+                               a["out"], a["st"], None)
+
+
+def test_device_geometry_refusals(lib):
+    def pw(**kw):
+        return pool_window(lib, **kw)
+    assert pw(nb=0) == OK
+    for k in ("raw", "w", "dt", "out", "st"):
+        assert pw(**{k: None}) == NULL, k
+    assert pw(nb=-1) == EXTENT and pw(mt=-4) == EXTENT
+    assert pw(nb=1025) == EXTENT
+    assert pw(ks=127) == STRIDE
+    assert pw(rd=3) == PARAM
+    assert pw(mt=262148, nb=1) == CAP
+    # prep / score / select with a device count refuse like their host-count twins, and need the word
+    assert lib.qsa_prep_queries_dev(P, 512, P, 8, P, 64, 1e4, 1e-6, None, 4096, P, P, None) == NULL
+    assert lib.qsa_prep_queries_dev(P, 500, P, 8, P, 64, 1e4, 1e-6, P, 4096, P, P, None) == STRIDE
+    assert lib.qsa_prep_queries_dev(P, 512, P, 0, P, 64, 1e4, 1e-6, None, 4096, P, P, None) == OK
+    assert lib.qsa_score_prepped_dev(P, P, 8, P, None, 4096, P, 1024, 8 * 1024, P, None) == NULL
+    assert lib.qsa_score_prepped_dev(P, P, 8, P, P, 4096, P, 1023, 8 * 1024, P, None) == STRIDE
+    assert lib.qsa_score_prepped_dev(P, P, 8, P, P, 4096, P, 1024, 8 * 1024 - 1, P, None) == CAP
+    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 8, None, 4096, 2048, P, 2051, P, P, None) == NULL
+    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 8, P, 4096, 2046, P, 2051, P, P, None) == BUDGET
+    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 8, P, 4096, 2048, P, 2050, P, P, None) == STRIDE
+    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 0, None, 4096, 2048, P, 2051, P, P, None) == OK
 
 
 def prep(lib, **kw):

@@ -1,0 +1,166 @@
+"""A graph-capturable decode step: pool_window -> prep_dev -> score_dev ->
+select_indices_dev -> gather, with the live cache length in a device word.
+
+Checked against the host-count calls (each of which is held to the oracle by
+the other GPU tests): eagerly at several lengths, then as one captured HIP
+graph replayed while the cache grows, with eager work and synchronisation
+between replays and every replay compared."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_token_qsa_amd as qsa
+from tests.gpu_util import DEV, note, workload
+
+pytestmark = pytest.mark.gpu
+
+CEIL = 65536 + 256
+ROWS = 4
+BUDGET = 2048
+WINDOW = 4       # blocks re-pooled per step: covers up to 16 new tokens
+KV_DIM, PAGE = 64, 16
+
+
+class Setup:
+    def __init__(self):
+        w = workload(3)
+        self.w = w
+        g = torch.Generator().manual_seed(4321)
+        raw = torch.randn((CEIL, 128), generator=g).to(torch.bfloat16)
+        self.raw = raw.view(torch.int16).to(DEV)
+        self.wk = torch.from_numpy(w["k_norm_w"].view(np.int16)).to(DEV)
+        self.wq = torch.from_numpy(w["q_norm_w"].view(np.int16)).to(DEV)
+        self.q = torch.from_numpy(w["queries"][:ROWS].reshape(ROWS, 512).view(np.int16)).to(DEV)
+        n_pages = CEIL // PAGE
+        self.kc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE, KV_DIM), dtype=torch.int16, generator=g).to(DEV)
+        self.vc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE, KV_DIM), dtype=torch.int16, generator=g).to(DEV)
+        self.table = torch.randperm(n_pages, generator=g).to(torch.int32).to(DEV)
+        self.n_pages = n_pages
+        self.slots = -(-(BUDGET + 3) // PAGE) * PAGE
+
+    def rope(self):
+        w = self.w
+        return w["rotary_dim"], w["theta"], w["eps"]
+
+    def buffers(self):
+        b = {
+            "pooled": torch.zeros((CEIL // 4, 128), dtype=torch.int16, device=DEV),
+            "qhat": torch.zeros((ROWS, 4, 128), dtype=torch.int16, device=DEV),
+            "scores": torch.zeros(ROWS * (CEIL // 4), dtype=torch.float32, device=DEV),
+            "idx": torch.full((ROWS, BUDGET + 3), -5, dtype=torch.int32, device=DEV),
+            "counts": torch.zeros(ROWS, dtype=torch.int32, device=DEV),
+            "ko": torch.zeros((ROWS, self.slots, KV_DIM), dtype=torch.int16, device=DEV),
+            "vo": torch.zeros((ROWS, self.slots, KV_DIM), dtype=torch.int16, device=DEV),
+            "tab": torch.zeros((ROWS, self.slots // PAGE), dtype=torch.int32, device=DEV),
+            "st": torch.zeros(1, dtype=torch.int32, device=DEV),
+            "pos": torch.zeros(ROWS, dtype=torch.int32, device=DEV),
+            "dt": torch.zeros(1, dtype=torch.int32, device=DEV),
+        }
+        return b
+
+    def reference(self, T):
+        """The host-count path at cache length T: every complete block pooled,
+        rows at position T - 1."""
+        rd, th, eps = self.rope()
+        b = self.buffers()
+        b["pos"].fill_(T - 1)
+        qsa.qsa_pool_keys(self.raw[:T], self.wk, rd, th, eps, b["pooled"])
+        qsa.qsa_prep_queries(self.q, b["pos"], self.wq, rd, th, eps, T, b["qhat"], b["st"])
+        qsa.qsa_score_prepped(b["qhat"], b["pos"], b["pooled"], T, b["scores"], CEIL // 4, b["st"])
+        qsa.qsa_select_indices(b["scores"], CEIL // 4, b["pos"], T, BUDGET, b["idx"], b["counts"], b["st"])
+        qsa.qsa_gather_kv(self.kc, self.vc, self.table, 0, self.n_pages, b["idx"], b["counts"], b["ko"], b["vo"],
+                          b["tab"], b["st"])
+        torch.cuda.synchronize()
+        return b
+
+    def step(self, b):
+        """The device-geometry step; reads T from b["dt"] and positions from b["pos"]."""
+        rd, th, eps = self.rope()
+        qsa.qsa_pool_window(self.raw, self.wk, rd, th, eps, b["dt"], WINDOW, b["pooled"], b["st"])
+        qsa.qsa_prep_queries_dev(self.q, b["pos"], self.wq, rd, th, eps, b["dt"], CEIL, b["qhat"], b["st"])
+        qsa.qsa_score_prepped_dev(b["qhat"], b["pos"], b["pooled"], b["dt"], CEIL, b["scores"], CEIL // 4, b["st"])
+        qsa.qsa_select_indices_dev(b["scores"], CEIL // 4, b["pos"], b["dt"], CEIL, BUDGET, b["idx"], b["counts"],
+                                   b["st"])
+        qsa.qsa_gather_kv(self.kc, self.vc, self.table, 0, self.n_pages, b["idx"], b["counts"], b["ko"], b["vo"],
+                          b["tab"], b["st"])
+
+
+def assert_same(got, ref, T, label):
+    n = T // 4
+    pooled_ok = torch.equal(got["pooled"][:n], ref["pooled"][:n])
+    sc_g = got["scores"].view(ROWS, CEIL // 4)[:, :n]
+    sc_r = ref["scores"].view(ROWS, CEIL // 4)[:, :n]
+    assert pooled_ok, f"{label}: pooled keys differ at T={T}"
+    assert torch.equal(got["qhat"], ref["qhat"]), f"{label}: prepared queries differ at T={T}"
+    assert torch.equal(sc_g.view(torch.int32), sc_r.view(torch.int32)), f"{label}: scores differ at T={T}"
+    assert torch.equal(got["idx"], ref["idx"]) and torch.equal(got["counts"], ref["counts"]), \
+        f"{label}: index lists differ at T={T}"
+    for k in ("ko", "vo", "tab"):
+        assert torch.equal(got[k], ref[k]), f"{label}: {k} differs at T={T}"
+
+
+def test_device_geometry_calls_equal_host_count_calls():
+    s = Setup()
+    b = s.buffers()
+    T0 = CEIL - 200
+    rd, th, eps = s.rope()
+    qsa.qsa_pool_keys(s.raw[:T0 - 1], s.wk, rd, th, eps, b["pooled"])  # the cache before the first step
+    for T in (T0, T0 + 1, T0 + 2, T0 + 3, T0 + 4, T0 + 11, T0 + 27):
+        note(f"device geometry, eager: T={T}")
+        b["dt"].fill_(T)
+        b["pos"].fill_(T - 1)
+        b["st"].zero_()
+        s.step(b)
+        torch.cuda.synchronize()
+        assert int(b["st"].item()) == 0
+        assert_same(b, s.reference(T), T, "eager")
+
+
+def test_captured_decode_step_replays_as_the_cache_grows():
+    s = Setup()
+    b = s.buffers()
+    T0 = CEIL - 120
+    rd, th, eps = s.rope()
+    qsa.qsa_pool_keys(s.raw[:T0 - 1], s.wk, rd, th, eps, b["pooled"])
+    b["dt"].fill_(T0)
+    b["pos"].fill_(T0 - 1)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        s.step(b)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note("capturing the decode step")
+    with torch.cuda.graph(graph):
+        s.step(b)
+    torch.cuda.synchronize()
+    T = T0
+    for k, add in enumerate((0, 1, 1, 1, 1, 3, 5, 16, 2, 1)):
+        T += add
+        note(f"replay {k}: T={T}")
+        b["dt"].fill_(T)
+        b["pos"].fill_(T - 1)
+        b["st"].zero_()
+        b["idx"].fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(b["st"].item()) == 0
+        assert_same(b, s.reference(T), T, f"replay {k}")
+
+
+def test_device_count_past_the_ceiling_is_clamped_and_flagged():
+    s = Setup()
+    b = s.buffers()
+    rd, th, eps = s.rope()
+    qsa.qsa_pool_keys(s.raw, s.wk, rd, th, eps, b["pooled"])
+    b["dt"].fill_(CEIL + 9)
+    b["pos"].fill_(CEIL - 1)
+    s.step(b)
+    torch.cuda.synchronize()
+    assert int(b["st"].item()) == qsa.STATUS_BAD_GEOMETRY
+    ref = s.reference(CEIL)
+    assert torch.equal(b["idx"], ref["idx"]) and torch.equal(b["ko"], ref["ko"])
