@@ -445,6 +445,7 @@ def decode_next(d: Device, torch, qsa):
                      torch)
     if qsa.check_status(d.status) != 0:
         raise RuntimeError("device status set in the decode gather")
+    graph_fig = decode_graph(d, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab)
     n_sel = int(counts.sum().item())
     alg = 4 * KV_DIM * n_sel + 4 * KV_DIM * d.rows * slots + 4 * d.rows * (stride + 1 + slots // PAGE_SIZE)
     gbs = alg / (g_us * 1e-6) / 1e9
@@ -452,7 +453,44 @@ def decode_next(d: Device, torch, qsa):
     return {"select_indices_us": sel_us,
             "kv_gather": {"us": g_us, "kv_dim": KV_DIM, "page_size": PAGE_SIZE, "slots": slots,
                           "entries": n_sel, "alg_bytes": alg, "achieved_GBs": round(gbs, 1),
-                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "decode_step": graph_fig}
+
+
+def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab):
+    """One production decode step with the cache length in a device word:
+    pool the block the new token completed, prep, score, index-list select,
+    K/V gather.  Timed as eager launches and as one captured HIP graph
+    replayed back to back (positions and cache fixed; each replay redoes the
+    same step)."""
+    w = d.w
+    rd, th, eps = w["rotary_dim"], w["theta"], w["eps"]
+    dt = torch.full((1,), d.T, dtype=torch.int32, device="cuda:0")
+
+    def step():
+        qsa.qsa_pool_window(d.raw, d.wk, rd, th, eps, dt, 1, d.pooled, d.status)
+        qsa.qsa_prep_queries_dev(d.q, d.pos, d.wq, rd, th, eps, dt, d.T, d.qhat, d.status)
+        qsa.qsa_score_prepped_dev(d.qhat, d.pos, d.pooled, dt, d.T, d.scores, d.cols, d.status)
+        qsa.qsa_select_indices_dev(d.scores, d.cols, d.pos, dt, d.T, w["budget"], idx, counts, d.status)
+        qsa.qsa_gather_kv(kc, vc, table, 0, n_pages, idx, counts, ko, vo, otab, d.status)
+
+    eager_us = launch_us(step, torch)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    replay_us = launch_us(graph.replay, torch)
+    if qsa.check_status(d.status) != 0:
+        raise RuntimeError("device status set in the captured decode step")
+    del graph
+    return {"stages": "pool_window(1 block) + prep + score + select_indices + gather",
+            "eager_us": eager_us, "graph_replay_us": replay_us}
 
 
 def fused_prefill(d: Device, torch, qsa):
