@@ -428,8 +428,8 @@ def decode_next(d: Device, torch, qsa):
     d.pool()
     d.prep()
     d.score()
-    sel_us = launch_us(lambda: qsa.qsa_select_indices(d.scores, d.cols, d.pos, d.T, budget, idx, counts,
-                                                      d.status), torch)
+    sel_us = launch_us(lambda: qsa.qsa_select_indices_ws(d.scores, d.cols, d.pos, d.T, budget, idx, counts,
+                                                         d.status, d.ws), torch)
     n_pages = -(-d.T // PAGE_SIZE)
     g = torch.Generator(device="cuda:0")
     g.manual_seed(1000 + int(w.get("wid", 0)))
@@ -471,7 +471,7 @@ def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko,
         qsa.qsa_pool_window(d.raw, d.wk, rd, th, eps, dt, 1, d.pooled, d.status)
         qsa.qsa_prep_queries_dev(d.q, d.pos, d.wq, rd, th, eps, dt, d.T, d.qhat, d.status)
         qsa.qsa_score_prepped_dev(d.qhat, d.pos, d.pooled, dt, d.T, d.scores, d.cols, d.status)
-        qsa.qsa_select_indices_dev(d.scores, d.cols, d.pos, dt, d.T, w["budget"], idx, counts, d.status)
+        qsa.qsa_select_indices_dev(d.scores, d.cols, d.pos, dt, d.T, w["budget"], idx, counts, d.status, d.ws)
         qsa.qsa_gather_kv(kc, vc, table, 0, n_pages, idx, counts, ko, vo, otab, d.status)
 
     eager_us = launch_us(step, torch)

@@ -210,7 +210,8 @@ int qsa_select_indices(const float* scores, int64_t score_cols, int64_t scores_l
                        void* stream);
 
 /*
- * qsa_select_workspace_bytes -- device workspace qsa_select_mask_ws needs for
+ * qsa_select_workspace_bytes -- device workspace qsa_select_mask_ws (and the
+ * index-list forms qsa_select_indices_ws / _dev) needs for
  * `rows` rows over a `tokens`-token cache: 0 when it selects one workgroup
  * per row (more than 128 rows, or caches of at most 65536 + 3 tokens), else
  * 4352 bytes per 16384 tokens (rounded up) per row.  Negative QSA_ERR_EXTENT /
@@ -366,12 +367,30 @@ int qsa_score_prepped_dev(const uint16_t* qhat, const int32_t* pos, int64_t rows
                           float* scores, int64_t score_cols, int64_t scores_len,
                           int32_t* dev_status, void* stream);
 
-/* qsa_select_indices with the live cache length on the device; the index
- * lists do not depend on the cache length beyond the validity of pos. */
+/* qsa_select_indices_ws with the live cache length on the device; the index
+ * lists do not depend on the cache length beyond the validity of pos.  The
+ * workspace rules use max_tokens: qsa_select_workspace_bytes(rows,
+ * max_tokens) bytes. */
 int qsa_select_indices_dev(const float* scores, int64_t score_cols, int64_t scores_len,
                            const int32_t* pos, int64_t rows, const int32_t* dev_tokens,
                            int64_t max_tokens, int64_t budget, int32_t* idx, int64_t idx_stride,
-                           int32_t* counts, int32_t* dev_status, void* stream);
+                           int32_t* counts, int32_t* dev_status, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
+/*
+ * qsa_select_indices_ws -- qsa_select_indices, same lists and counts, with
+ * the split form of qsa_select_mask_ws for batches of few long rows: when
+ * qsa_select_workspace_bytes(rows, tokens) > 0, the chunks' local top lists
+ * go to the workspace and one workgroup per (row, 16384-token slice) writes
+ * the slice's kept tokens at the position the earlier slices' kept blocks
+ * leave free.  Otherwise it is qsa_select_indices and ignores the workspace.
+ * Arguments and refusals: those of qsa_select_indices, and the workspace
+ * rules of qsa_select_mask_ws.
+ */
+int qsa_select_indices_ws(const float* scores, int64_t score_cols, int64_t scores_len,
+                          const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                          int32_t* idx, int64_t idx_stride, int32_t* counts, int32_t* dev_status,
+                          void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * qsa_rope_inv_freq -- host only: the rotary frequencies the kernels use,

@@ -23,7 +23,7 @@ __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_pre
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
            "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
-           "qsa_select_indices_dev",
+           "qsa_select_indices_dev", "qsa_select_indices_ws",
            "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
@@ -371,10 +371,40 @@ def qsa_score_prepped_dev(qhat: torch.Tensor, pos: torch.Tensor, pooled: torch.T
                                      _stream_ptr(stream)), "qsa_score_prepped_dev")
 
 
+def _workspace(workspace):
+    if workspace is None:
+        return 0
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
+    return workspace.numel() * workspace.element_size()
+
+
+def qsa_select_indices_ws(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, tokens: int,
+                          budget: int, idx: torch.Tensor, counts: torch.Tensor, dev_status: torch.Tensor,
+                          workspace: torch.Tensor | None, stream=None) -> None:
+    """qsa_select_indices, split over workgroups for few long rows; `workspace`
+    holds qsa_select_workspace_bytes(rows, tokens) bytes (None when 0)."""
+    _dev(scores, "scores", (torch.float32,))
+    _dev(pos, "pos", (torch.int32,))
+    _dev(idx, "idx", (torch.int32,))
+    _dev(counts, "counts", (torch.int32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous() and scores.is_contiguous(), "pos and scores must be contiguous")
+    idx_stride = _rows_2d(idx, "idx", budget + RATIO - 1)
+    _need(idx.shape[0] >= rows, "idx needs a row per position")
+    _need(counts.is_contiguous() and counts.numel() >= rows, "counts must be contiguous [rows]")
+    lib = load()
+    _check(lib.qsa_select_indices_ws(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens, budget,
+                                     _ptr(idx), idx_stride, _ptr(counts), _ptr(dev_status), _ptr(workspace),
+                                     _workspace(workspace), _stream_ptr(stream)), "qsa_select_indices_ws")
+
+
 def qsa_select_indices_dev(scores: torch.Tensor, score_cols: int, pos: torch.Tensor,
                            dev_tokens: torch.Tensor, max_tokens: int, budget: int, idx: torch.Tensor,
-                           counts: torch.Tensor, dev_status: torch.Tensor, stream=None) -> None:
-    """qsa_select_indices with the live cache length in dev_tokens[0]."""
+                           counts: torch.Tensor, dev_status: torch.Tensor, workspace: torch.Tensor | None = None,
+                           stream=None) -> None:
+    """qsa_select_indices_ws with the live cache length in dev_tokens[0];
+    `workspace` holds qsa_select_workspace_bytes(rows, max_tokens) bytes."""
     _dev(scores, "scores", (torch.float32,))
     _dev(pos, "pos", (torch.int32,))
     _dev(idx, "idx", (torch.int32,))
@@ -389,7 +419,8 @@ def qsa_select_indices_dev(scores: torch.Tensor, score_cols: int, pos: torch.Ten
     lib = load()
     _check(lib.qsa_select_indices_dev(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, _ptr(dev_tokens),
                                       max_tokens, budget, _ptr(idx), idx_stride, _ptr(counts), _ptr(dev_status),
-                                      _stream_ptr(stream)), "qsa_select_indices_dev")
+                                      _ptr(workspace), _workspace(workspace), _stream_ptr(stream)),
+           "qsa_select_indices_dev")
 
 
 def qsa_rope_inv_freq(rotary_dim: int, rope_theta: float) -> list:

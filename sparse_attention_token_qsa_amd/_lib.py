@@ -36,7 +36,8 @@ EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_pre
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
            "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
-           "qsa_select_indices_dev", "qsa_rope_inv_freq", "qsa_strerror", "qsa_abi_version")
+           "qsa_select_indices_dev", "qsa_select_indices_ws", "qsa_rope_inv_freq", "qsa_strerror",
+           "qsa_abi_version")
 ABI_VERSION = 7
 
 _lib = None
@@ -89,8 +90,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_prep_queries_dev.restype = ctypes.c_int
     lib.qsa_score_prepped_dev.argtypes = [P, P, I64, P, P, I64, P, I64, I64, P, P]
     lib.qsa_score_prepped_dev.restype = ctypes.c_int
-    lib.qsa_select_indices_dev.argtypes = [P, I64, I64, P, I64, P, I64, I64, P, I64, P, P, P]
+    lib.qsa_select_indices_dev.argtypes = [P, I64, I64, P, I64, P, I64, I64, P, I64, P, P, P, I64, P]
     lib.qsa_select_indices_dev.restype = ctypes.c_int
+    lib.qsa_select_indices_ws.argtypes = [P, I64, I64, P, I64, I64, I64, P, I64, P, P, P, I64, P]
+    lib.qsa_select_indices_ws.restype = ctypes.c_int
     lib.qsa_rope_inv_freq.argtypes = [I32, F, P]
     lib.qsa_rope_inv_freq.restype = ctypes.c_int
     lib.qsa_strerror.argtypes = [ctypes.c_int]

@@ -352,27 +352,67 @@ int qsa_score_prepped_dev(const uint16_t* qhat, const int32_t* pos, int64_t rows
                                                  dev_status, static_cast<hipStream_t>(stream), dev_tokens));
 }
 
-int qsa_select_indices_dev(const float* scores, int64_t score_cols, int64_t scores_len,
-                           const int32_t* pos, int64_t rows, const int32_t* dev_tokens,
-                           int64_t max_tokens, int64_t budget, int32_t* idx, int64_t idx_stride,
-                           int32_t* counts, int32_t* dev_status, void* stream) {
-  if (dev_tokens == nullptr && rows > 0 && max_tokens > 0) return QSA_ERR_NULL;
-  if (rows < 0 || max_tokens < 0 || score_cols < 0 || scores_len < 0 || idx_stride < 0) return QSA_ERR_EXTENT;
+namespace {
+// Refusals of the index-list selectors (host checks only); 1 = valid, not empty.
+int check_indices(const float* scores, int64_t score_cols, int64_t scores_len, const int32_t* pos,
+                  int64_t rows, int64_t tokens, int64_t budget, int32_t* idx, int64_t idx_stride,
+                  int32_t* counts, int32_t* dev_status) {
+  if (rows < 0 || tokens < 0 || score_cols < 0 || scores_len < 0 || idx_stride < 0) return QSA_ERR_EXTENT;
   if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)
     return QSA_ERR_BUDGET;
-  if (score_cols < max_tokens / QSA_RATIO) return QSA_ERR_STRIDE;
+  if (score_cols < tokens / QSA_RATIO) return QSA_ERR_STRIDE;
   if (idx_stride < budget + QSA_RATIO - 1) return QSA_ERR_STRIDE;
-  if (max_tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
+  if (tokens > QSA_MAX_TOKENS) return QSA_ERR_CAPACITY;
   int64_t need;
   if (mul_overflows(rows, score_cols, &need) || scores_len < need) return QSA_ERR_CAPACITY;
   if (mul_overflows(rows, idx_stride, &need)) return QSA_ERR_CAPACITY;
   if (rows > INT32_MAX) return QSA_ERR_CAPACITY;
-  if (rows == 0 || max_tokens == 0) return QSA_OK;
+  if (rows == 0 || tokens == 0) return QSA_OK;
   if (pos == nullptr || idx == nullptr || counts == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
-  if (max_tokens >= QSA_RATIO && scores == nullptr) return QSA_ERR_NULL;
-  return launch_status(qsa::launch_select_indices(scores, score_cols, pos, rows, max_tokens,
-                                                  static_cast<int>(budget / QSA_RATIO), idx, idx_stride, counts,
-                                                  dev_status, static_cast<hipStream_t>(stream), dev_tokens));
+  if (tokens >= QSA_RATIO && scores == nullptr) return QSA_ERR_NULL;
+  return 1;
+}
+
+// The one-workgroup-per-row or the split index-list selector.
+int launch_indices(const float* scores, int64_t score_cols, const int32_t* pos, int64_t rows, int64_t tokens,
+                   int64_t budget, int32_t* idx, int64_t idx_stride, int32_t* counts, int32_t* dev_status,
+                   void* workspace, int64_t workspace_bytes, void* stream, const int32_t* dev_tokens) {
+  if (workspace_bytes < 0) return QSA_ERR_EXTENT;
+  const int keep_max = static_cast<int>(budget / QSA_RATIO);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!qsa::select_split_pays(rows, tokens))
+    return launch_status(qsa::launch_select_indices(scores, score_cols, pos, rows, tokens, keep_max, idx,
+                                                    idx_stride, counts, dev_status, s, dev_tokens));
+  if (workspace == nullptr) return QSA_ERR_NULL;
+  if (workspace_bytes < qsa::select_split_workspace_bytes(rows, tokens)) return QSA_ERR_CAPACITY;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return QSA_ERR_PARAM;
+  return launch_status(qsa::launch_select_split_indices(scores, score_cols, pos, rows, tokens, keep_max, idx,
+                                                        idx_stride, counts, dev_status, workspace, s, dev_tokens));
+}
+}  // namespace
+
+int qsa_select_indices_ws(const float* scores, int64_t score_cols, int64_t scores_len,
+                          const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                          int32_t* idx, int64_t idx_stride, int32_t* counts, int32_t* dev_status,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+  const int rc = check_indices(scores, score_cols, scores_len, pos, rows, tokens, budget, idx, idx_stride,
+                               counts, dev_status);
+  if (rc <= 0) return rc;
+  return launch_indices(scores, score_cols, pos, rows, tokens, budget, idx, idx_stride, counts, dev_status,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int qsa_select_indices_dev(const float* scores, int64_t score_cols, int64_t scores_len,
+                           const int32_t* pos, int64_t rows, const int32_t* dev_tokens,
+                           int64_t max_tokens, int64_t budget, int32_t* idx, int64_t idx_stride,
+                           int32_t* counts, int32_t* dev_status, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  const int rc = check_indices(scores, score_cols, scores_len, pos, rows, max_tokens, budget, idx, idx_stride,
+                               counts, dev_status);
+  if (rc <= 0) return rc;
+  if (dev_tokens == nullptr) return QSA_ERR_NULL;
+  return launch_indices(scores, score_cols, pos, rows, max_tokens, budget, idx, idx_stride, counts, dev_status,
+                        workspace, workspace_bytes, stream, dev_tokens);
 }
 
 }  // extern "C"

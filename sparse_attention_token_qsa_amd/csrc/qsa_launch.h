@@ -53,6 +53,12 @@ int64_t select_split_workspace_bytes(int64_t rows, int64_t tokens);
 hipError_t launch_select_split(const float* scores, int64_t score_cols, const int32_t* pos,
                                int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                                int32_t* status, void* workspace, hipStream_t stream);
+// The same split, writing index lists (qsa_select_indices' format).
+hipError_t launch_select_split_indices(const float* scores, int64_t score_cols, const int32_t* pos,
+                                       int64_t rows, int64_t tokens, int keep_max, int32_t* idx,
+                                       int64_t idx_stride, int32_t* counts, int32_t* status,
+                                       void* workspace, hipStream_t stream,
+                                       const int32_t* dev_tokens = nullptr);
 
 // One-workgroup-per-row selector over the rows whose row_flag is nonzero
 // only (the others are left untouched): the fused path's fallback.

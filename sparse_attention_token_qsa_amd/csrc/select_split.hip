@@ -38,9 +38,13 @@ struct SplitArgs {
   const float* scores;
   int64_t score_cols;
   const int32_t* pos;
-  int64_t tokens;
+  int64_t tokens;             // mask row length; the ceiling when dev_tokens is set
+  const int32_t* dev_tokens;  // optional live cache length on the device
   int keep_max;
   uint8_t* mask;
+  int32_t* idx;        // index mode: [rows, idx_stride] kept token indices
+  int64_t idx_stride;
+  int32_t* counts;     // index mode: [rows] entries written
   int32_t* status;
   uint64_t* cand;  // [rows][chunks][kMaxKeep] composites
   int32_t* cnt;    // [rows][chunks] composites emitted, -1 for a refused row
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
   const int chunk = static_cast<int>(blockIdx.x - row * a.chunks);
   const int64_t slot = row * a.chunks + chunk;
   const int64_t p = a.pos[row];
-  if (p < 0 || p >= a.tokens) {
+  if (p < 0 || p >= live_tokens(a.tokens, a.dev_tokens, a.status)) {
     if (tid == 0) {
       if (chunk == 0) atomicOr(a.status, QSA_STATUS_BAD_POSITION);
       a.cnt[slot] = -1;
@@ -252,7 +256,11 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
 }
 
 // ---- 2. the row's threshold from the union, and one slice of its mask ----
-template <bool VEC>
+// IDX: instead of the mask slice, the slice's part of the row's index list
+// (see select.hip's index mode): its kept blocks' tokens at the position the
+// kept blocks of the earlier chunks leave free; slice 0 also writes the
+// tail, the -1 fill and the count.
+template <bool VEC, bool IDX>
 __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
   constexpr int NT = 1024, NW = NT / 64;
   constexpr int KPT = 8;  // composites per thread: 16 chunks x 512 / 1024
@@ -262,6 +270,7 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
   __shared__ uint64_t lcand[kCandCap];
   __shared__ int cnts[64];
   __shared__ int offs[65];
+  __shared__ int kcount[64];  // index mode: kept blocks per chunk
   __shared__ __attribute__((aligned(16))) uint32_t keptbits[kSplitChunk / 32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -275,7 +284,22 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
 
   // this slice's bytes: block bytes from keptbits (kept = 1), the rest 1 for
   // t <= last, 0 otherwise
+  const int cap = 4 * a.keep_max + 3;  // index mode: entries per row
+  int32_t* irow = IDX ? a.idx + row * a.idx_stride : nullptr;
+  // index mode, rows without a selection: entries i <= last are i (this
+  // slice's tokens), and slice 0 writes the -1 fill and the count
+  auto write_prefix_idx = [&](int64_t last) {
+    for (int64_t t = t_begin + tid; t < t_end && t <= last; t += NT) irow[t] = static_cast<int32_t>(t);
+    if (slice == 0) {
+      for (int i = static_cast<int>(last + 1) + tid; i < cap; i += NT) irow[i] = -1;
+      if (tid == 0) a.counts[row] = static_cast<int32_t>(last + 1);
+    }
+  };
   auto write_slice = [&](int n, int64_t last, bool use_bits) {
+    if constexpr (IDX) {
+      write_prefix_idx(use_bits ? -1 : last);  // never called with use_bits in index mode
+      return;
+    }
     const int blk0 = slice * kSplitChunk;
     if constexpr (VEC) {
       for (int64_t c = t_begin / 16 + tid; c < t_end / 16; c += NT) {
@@ -307,12 +331,13 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
     }
   };
 
-  if (p < 0 || p >= T) {
+  if (p < 0 || p >= live_tokens(T, a.dev_tokens, nullptr)) {
     write_slice(0, -1, false);
     return;
   }
   const int n = static_cast<int>((p + 1) / kRatio);
   if (tid < a.chunks) cnts[tid] = a.cnt[row * a.chunks + tid];
+  if (tid < 64) kcount[tid] = 0;
   if (tid < kSplitChunk / 32) keptbits[tid] = 0u;
   if (tid < 256) hist[tid] = 0u;
   __syncthreads();
@@ -445,9 +470,40 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
       const int lb = b - blk0;
       atomicOr(&keptbits[lb >> 5], 1u << (lb & 31));
     }
+    if constexpr (IDX)
+      if (kept) atomicAdd(&kcount[b / kSplitChunk], 1);
   }
   __syncthreads();
-  write_slice(n, p, true);
+  if constexpr (!IDX) {
+    write_slice(n, p, true);
+  } else {
+    // this slice's kept blocks follow those of the earlier chunks, ascending
+    int before = 0;
+    for (int c = 0; c < slice; ++c) before += kcount[c];
+    constexpr int kWords = kSplitChunk / 32;
+    const uint32_t word = tid < kWords ? keptbits[tid] : 0u;
+    const uint32_t pc = static_cast<uint32_t>(__popc(word));
+    const uint32_t incl = wave_incl_sum(pc);  // waves 0 and 1 hold the 128 words
+    if (lane == 63 && wave < 2) red[wave] = incl;
+    __syncthreads();
+    uint32_t rank = incl - pc + (wave == 1 ? red[0] : 0u);
+    uint32_t wb = word;
+    while (wb != 0u) {
+      const int bit = __ffs(wb) - 1;
+      wb &= wb - 1u;
+      const int b = blk0 + 32 * tid + bit;
+      const int at = 4 * (before + static_cast<int>(rank));
+#pragma unroll
+      for (int k = 0; k < kRatio; ++k) irow[at + k] = kRatio * b + k;
+      ++rank;
+    }
+    if (slice == 0) {
+      const int tail = static_cast<int>(p + 1) - kRatio * n;
+      for (int i = tid; i < cap - 4 * keep; i += NT)
+        irow[4 * keep + i] = i < tail ? kRatio * n + i : -1;
+      if (tid == 0) a.counts[row] = 4 * keep + tail;
+    }
+  }
 }
 
 }  // namespace
@@ -468,6 +524,37 @@ bool select_split_pays(int64_t rows, int64_t tokens) {
   return tokens / kRatio > 4 * kSplitChunk && rows <= 128;
 }
 
+namespace {
+
+hipError_t launch_split(SplitArgs a, int64_t rows, bool idx_mode, void* workspace, hipStream_t stream) {
+  const int64_t chunks = select_split_chunks(a.tokens);
+  if (chunks > 64 || rows * chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  a.chunks = static_cast<int>(chunks);
+  // candidates first (16-byte aligned), then the per-chunk counts
+  a.cand = static_cast<uint64_t*>(workspace);
+  a.cnt = reinterpret_cast<int32_t*>(a.cand + rows * chunks * kMaxKeep);
+  const dim3 grid(static_cast<unsigned>(rows * chunks));
+  const bool svec = (a.score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
+  if (svec)
+    select_chunk_kernel<true><<<grid, dim3(512), 0, stream>>>(a);
+  else
+    select_chunk_kernel<false><<<grid, dim3(512), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (idx_mode) {
+    select_merge_kernel<false, true><<<grid, dim3(1024), 0, stream>>>(a);
+  } else {
+    const bool mvec = (a.tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(a.mask) % 16 == 0);
+    if (mvec)
+      select_merge_kernel<true, false><<<grid, dim3(1024), 0, stream>>>(a);
+    else
+      select_merge_kernel<false, false><<<grid, dim3(1024), 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_select_split(const float* scores, int64_t score_cols, const int32_t* pos,
                                int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                                int32_t* status, void* workspace, hipStream_t stream) {
@@ -479,26 +566,25 @@ hipError_t launch_select_split(const float* scores, int64_t score_cols, const in
   a.keep_max = keep_max;
   a.mask = mask;
   a.status = status;
-  const int64_t chunks = select_split_chunks(tokens);
-  if (chunks > 64 || rows * chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  a.chunks = static_cast<int>(chunks);
-  // candidates first (16-byte aligned), then the per-chunk counts
-  a.cand = static_cast<uint64_t*>(workspace);
-  a.cnt = reinterpret_cast<int32_t*>(a.cand + rows * chunks * kMaxKeep);
-  const dim3 grid(static_cast<unsigned>(rows * chunks));
-  const bool svec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
-  if (svec)
-    select_chunk_kernel<true><<<grid, dim3(512), 0, stream>>>(a);
-  else
-    select_chunk_kernel<false><<<grid, dim3(512), 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const bool mvec = (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
-  if (mvec)
-    select_merge_kernel<true><<<grid, dim3(1024), 0, stream>>>(a);
-  else
-    select_merge_kernel<false><<<grid, dim3(1024), 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_split(a, rows, false, workspace, stream);
+}
+
+hipError_t launch_select_split_indices(const float* scores, int64_t score_cols, const int32_t* pos,
+                                       int64_t rows, int64_t tokens, int keep_max, int32_t* idx,
+                                       int64_t idx_stride, int32_t* counts, int32_t* status,
+                                       void* workspace, hipStream_t stream, const int32_t* dev_tokens) {
+  SplitArgs a{};
+  a.scores = scores;
+  a.score_cols = score_cols;
+  a.pos = pos;
+  a.tokens = tokens;
+  a.dev_tokens = dev_tokens;
+  a.keep_max = keep_max;
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.counts = counts;
+  a.status = status;
+  return launch_split(a, rows, true, workspace, stream);
 }
 
 }  // namespace qsa

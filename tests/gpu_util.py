@@ -134,3 +134,19 @@ def gpu_select_indices(scores: np.ndarray, cols: int, pos, tokens: int, budget: 
     qsa.qsa_select_indices(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, idx, counts, st)
     s = qsa.check_status(st)
     return idx.cpu().numpy(), counts.cpu().numpy(), s
+
+
+def gpu_select_indices_ws(scores: np.ndarray, cols: int, pos, tokens: int, budget: int, stride=None,
+                          fill: int = 0x5A):
+    """qsa_select_indices_ws with a junk-filled workspace of exactly the
+    reported size: (idx read back, counts, status, workspace bytes)."""
+    rows = len(pos)
+    stride = budget + 3 if stride is None else stride
+    idx = torch.full((rows, stride), -77, dtype=torch.int32, device=DEV)
+    counts = torch.full((rows,), -77, dtype=torch.int32, device=DEV)
+    st = status_word()
+    nbytes = qsa.qsa_select_workspace_bytes(rows, tokens)
+    ws = torch.full((max(nbytes, 16),), fill, dtype=torch.uint8, device=DEV) if nbytes else None
+    qsa.qsa_select_indices_ws(f32_dev(scores.reshape(-1)), cols, i32_dev(pos), tokens, budget, idx, counts, st, ws)
+    s = qsa.check_status(st)
+    return idx.cpu().numpy(), counts.cpu().numpy(), s, nbytes

@@ -310,10 +310,29 @@ def test_device_geometry_refusals(lib):
     assert lib.qsa_score_prepped_dev(P, P, 8, P, None, 4096, P, 1024, 8 * 1024, P, None) == NULL
     assert lib.qsa_score_prepped_dev(P, P, 8, P, P, 4096, P, 1023, 8 * 1024, P, None) == STRIDE
     assert lib.qsa_score_prepped_dev(P, P, 8, P, P, 4096, P, 1024, 8 * 1024 - 1, P, None) == CAP
-    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 8, None, 4096, 2048, P, 2051, P, P, None) == NULL
-    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 8, P, 4096, 2046, P, 2051, P, P, None) == BUDGET
-    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 8, P, 4096, 2048, P, 2050, P, P, None) == STRIDE
-    assert lib.qsa_select_indices_dev(P, 1024, 8 * 1024, P, 0, None, 4096, 2048, P, 2051, P, P, None) == OK
+    sid = lambda *a: lib.qsa_select_indices_dev(*a, None)  # noqa: E731
+    assert sid(P, 1024, 8 * 1024, P, 8, None, 4096, 2048, P, 2051, P, P, None, 0) == NULL
+    assert sid(P, 1024, 8 * 1024, P, 8, P, 4096, 2046, P, 2051, P, P, None, 0) == BUDGET
+    assert sid(P, 1024, 8 * 1024, P, 8, P, 4096, 2048, P, 2050, P, P, None, 0) == STRIDE
+    assert sid(P, 1024, 8 * 1024, P, 0, None, 4096, 2048, P, 2051, P, P, None, 0) == OK
+    # long rows need the split workspace
+    assert sid(P, 65536, 8 * 65536, P, 8, P, 262144, 2048, P, 2051, P, P, None, 0) == NULL
+    need = lib.qsa_select_workspace_bytes(8, 262144)
+    assert sid(P, 65536, 8 * 65536, P, 8, P, 262144, 2048, P, 2051, P, P, P, need - 1) == CAP
+    assert sid(P, 65536, 8 * 65536, P, 8, P, 262144, 2048, P, 2051, P, P, P + 8, need) == PARAM
+    assert sid(P, 65536, 8 * 65536, P, 8, P, 262144, 2048, P, 2051, P, P, P, -1) == EXTENT
+
+
+def test_select_indices_ws_refusals(lib):
+    siw = lambda *a: lib.qsa_select_indices_ws(*a, None)  # noqa: E731
+    assert siw(P, 16385, 8 * 16385, P, 0, 65540, 2048, P, 2051, P, P, None, 0) == OK
+    for i, name in ((0, "scores"), (3, "pos"), (7, "idx"), (9, "counts"), (10, "status"), (11, "ws")):
+        a = [P, 16385, 8 * 16385, P, 8, 65540, 2048, P, 2051, P, P, P, 1 << 20]
+        a[i] = None
+        assert siw(*a) == NULL, name
+    assert siw(P, 16385, 8 * 16385, P, 8, 65540, 2048, P, 2050, P, P, P, 1 << 20) == STRIDE
+    assert siw(P, 16385, 8 * 16385, P, 8, 65540, 2046, P, 2051, P, P, P, 1 << 20) == BUDGET
+    assert siw(P, 16385, 8 * 16385, P, 8, 65540, 2048, P, 2051, P, P, P, 8 * 5 * (4096 + 256) - 1) == CAP
 
 
 def prep(lib, **kw):

@@ -54,6 +54,8 @@ class Setup:
             "vo": torch.zeros((ROWS, self.slots, KV_DIM), dtype=torch.int16, device=DEV),
             "tab": torch.zeros((ROWS, self.slots // PAGE), dtype=torch.int32, device=DEV),
             "st": torch.zeros(1, dtype=torch.int32, device=DEV),
+            "ws": torch.full((max(qsa.qsa_select_workspace_bytes(ROWS, CEIL), 16),), 0x5A, dtype=torch.uint8,
+                             device=DEV),
             "pos": torch.zeros(ROWS, dtype=torch.int32, device=DEV),
             "dt": torch.zeros(1, dtype=torch.int32, device=DEV),
         }
@@ -81,7 +83,7 @@ class Setup:
         qsa.qsa_prep_queries_dev(self.q, b["pos"], self.wq, rd, th, eps, b["dt"], CEIL, b["qhat"], b["st"])
         qsa.qsa_score_prepped_dev(b["qhat"], b["pos"], b["pooled"], b["dt"], CEIL, b["scores"], CEIL // 4, b["st"])
         qsa.qsa_select_indices_dev(b["scores"], CEIL // 4, b["pos"], b["dt"], CEIL, BUDGET, b["idx"], b["counts"],
-                                   b["st"])
+                                   b["st"], b["ws"])
         qsa.qsa_gather_kv(self.kc, self.vc, self.table, 0, self.n_pages, b["idx"], b["counts"], b["ko"], b["vo"],
                           b["tab"], b["st"])
 

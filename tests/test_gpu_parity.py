@@ -15,7 +15,8 @@ import torch
 import oracle as O
 import synth
 from tests.gpu_util import (DEV, gpu_pool, gpu_prep, gpu_scores, gpu_scores_prepped, gpu_select,
-                            gpu_select_indices, gpu_select_ws, note, u16_dev, u16_host, workload)
+                            gpu_select_indices, gpu_select_indices_ws, gpu_select_ws, note, u16_dev, u16_host,
+                            workload)
 from tests.test_oracle_pins import check_structure
 
 pytestmark = pytest.mark.gpu
@@ -345,6 +346,75 @@ def test_select_ws_ragged_tokens_spare_columns_bad_positions(T):
     assert nbytes > 0
     assert gst == wst == O.STATUS_BAD_POSITION | O.STATUS_NONFINITE_SCORE
     assert np.array_equal(got, want)
+
+
+def _check_split_indices(sc, cols, pos, T, budget, stride=None):
+    stride = budget + 3 if stride is None else stride
+    want, wcnt, wst = O.select_indices(sc, cols, pos, T, budget)
+    got, gcnt, gst, nbytes = gpu_select_indices_ws(sc, cols, pos, T, budget, stride=stride)
+    assert gst == wst, (gst, wst)
+    assert np.array_equal(gcnt, wcnt), np.nonzero(gcnt != wcnt)[0][:8]
+    bad = [r for r in range(len(pos)) if not np.array_equal(got[r, : budget + 3], want[r])]
+    assert not bad, (budget, bad[:5], pos[bad[:5]])
+    assert np.all(got[:, budget + 3:] == -77), "wrote past budget + 3"
+    return nbytes, wst
+
+
+@pytest.mark.parametrize("wid", [3, 4])
+def test_select_indices_ws_on_oracle_scores_bit_exact(wid):
+    """Index lists through the split selector on the oracle's scores of the
+    decode workloads: equal to the oracle's lists and counts."""
+    w = workload(wid)
+    rows = sample_rows(wid)
+    T = w["tokens"]
+    cols = T // 4
+    note(f"split index lists on oracle scores: workload {wid}")
+    nbytes, st = _check_split_indices(dense(oracle_scores(wid, rows), cols), cols, w["pos"][rows], T, w["budget"])
+    assert (nbytes > 0) == (T > 65539) and st == 0
+
+
+@pytest.mark.parametrize("kind", ["zeros", "ties", "lowbyte", "wild", "equal", "random", "poison"])
+def test_select_indices_ws_fixtures_bit_exact(kind):
+    scores, cols, pos, T = synth.selector_fixture(kind)
+    note(f"split index lists fixture {kind}")
+    for budget in (2048, 64, 4):
+        nbytes, _ = _check_split_indices(scores, cols, pos, T, budget)
+        assert nbytes > 0
+
+
+def test_select_indices_ws_kept_blocks_in_one_chunk_and_across_boundaries():
+    T = 65536 + 4 * 4096 + 7
+    n = T // 4
+    pos = np.array([T - 1, T - 2, 4 * 8192 + 3, 4 * 4096 - 1, 4 * 4096 + 3, T - 1], dtype=np.int32)
+    sc = np.full((len(pos), n), np.nan, np.float32)
+    nb = (pos.astype(np.int64) + 1) // 4
+    sc[0, : nb[0]] = np.arange(nb[0], dtype=np.float32)
+    sc[1, : nb[1]] = 1.5
+    v = np.zeros(nb[2], np.float32)
+    v[4096 - 300: 4096 + 300] = 2.0
+    sc[2, : nb[2]] = v
+    rng = np.random.default_rng(5)
+    sc[3, : nb[3]] = rng.standard_normal(nb[3])
+    sc[4, : nb[4]] = rng.standard_normal(nb[4])
+    sc[5, : nb[5]] = -np.arange(nb[5], dtype=np.float32)
+    note(f"split index lists at chunk boundaries: tokens {T}")
+    for budget in (2048, 4):
+        _check_split_indices(sc, n, pos, T, budget, stride=budget + 11)
+
+
+@pytest.mark.parametrize("T", [65541, 131075, 262147])
+def test_select_indices_ws_ragged_tokens_bad_positions(T):
+    pos = np.array([T - 1, 0, 3, 4, 2051, T // 2, -1, T, 2 * T + 5, T - 3], dtype=np.int32)
+    cols = T // 4 + 3
+    scores = np.full((len(pos), cols), np.nan, np.float32)
+    rng = np.random.default_rng(T)
+    for r, p in enumerate(pos):
+        nn = (int(p) + 1) // 4 if 0 <= p < T else 0
+        scores[r, :nn] = rng.standard_normal(nn)
+    scores[9, 17] = np.inf
+    note(f"split index lists ragged: tokens {T}")
+    nbytes, st = _check_split_indices(scores, cols, pos, T, 2048, stride=2060)
+    assert nbytes > 0 and st == O.STATUS_BAD_POSITION | O.STATUS_NONFINITE_SCORE
 
 
 def test_select_ws_equals_select_and_reuses_its_workspace():
