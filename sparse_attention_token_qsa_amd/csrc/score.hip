@@ -924,7 +924,14 @@ hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
   // whose position is out of range even when no block is complete.
   int64_t n_tiles = (nb_total + G::TILE - 1) / G::TILE;
   if (n_tiles < 1) n_tiles = 1;
+  // About 1024 workgroups in all; but when few row groups would leave each
+  // workgroup a tile or two, keep at least D tiles per workgroup (the ring
+  // then overlaps its loads) as long as 256 workgroups remain.
   int64_t splits = (1024 + a.row_groups - 1) / a.row_groups;
+  const int64_t deep = n_tiles / D > (256 + a.row_groups - 1) / a.row_groups
+                           ? n_tiles / D
+                           : (256 + a.row_groups - 1) / a.row_groups;
+  if (splits > deep) splits = deep;
   if (splits < 1) splits = 1;
   if (splits > n_tiles) splits = n_tiles;
   a.splits = splits;
