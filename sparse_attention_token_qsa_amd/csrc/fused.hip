@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void cand_select_kernel(const CandArgs a) {
         const int b = static_cast<int>(4 * c + i);
         wv[i] = b < n ? (bit(b) ? 0x01010101u : 0u) : prefix_word(b, p);
       }
-      reinterpret_cast<uint4*>(mrow)[c] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      store_stream(reinterpret_cast<uint4*>(mrow) + c, wv[0], wv[1], wv[2], wv[3]);
     }
   } else {
     for (int64_t t2 = tid; t2 < T; t2 += NT) {

@@ -31,6 +31,8 @@
 //     separates the candidates, and `lowkey` excludes the non-candidates.
 //  3. Each thread writes its blocks' mask bytes (16 bytes per 4 blocks), the
 //     tail and the zero run from the same loop.
+// Scores are loaded and mask bytes stored as streaming (non-temporal) 16-byte
+// accesses: each is touched exactly once.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 #include "select_common.h"
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
 #pragma unroll
       for (int g = 0; g < KPT / 4; ++g) {
         const int q = tid + g * NT;
-        v[g] = s4[q < qlast ? q : qlast];
+        v[g] = load_stream(s4 + (q < qlast ? q : qlast));
       }
 #pragma unroll
       for (int g = 0; g < KPT / 4; ++g) {
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
           const uint32_t kk = opaque(key[4 * g + i]);
           wv[i] = b < n ? (kept(kk, b) ? 0x01010101u : 0u) : prefix_word(b, p);
         }
-        reinterpret_cast<uint4*>(mrow)[q] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        store_stream(reinterpret_cast<uint4*>(mrow) + q, wv[0], wv[1], wv[2], wv[3]);
       }
     }
   } else {
