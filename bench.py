@@ -35,8 +35,10 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU reaches its steady clocks only after ~100 ms of this load: with 5
+    # warm-up steps (2 ms) the timed steps measured 12% slower than at 300.
+    ap.add_argument("--steps", type=int, default=1000, help="timed steps (~0.35 s on the main workload)")
+    ap.add_argument("--warmup", type=int, default=300, help="untimed steps first")
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the decode and one-row figures")
