@@ -121,9 +121,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
   const int half = rd >> 1;
   const int64_t anchor = kRatio * b;
   for (int i = g; i < half; i += 16) {
-    float c, s;
-    rope_cos_sin(anchor, a.rp.inv_freq[i], c, s);
-    csq[slot][i] = f32_to_bf16(c) | (f32_to_bf16(s) << 16);
+    csq[slot][i] = rope_cos_sin_bf16x2(anchor, a.rp.inv_freq[i]);
   }
 
   // f32 mean of the 4 tokens in token order, cast to bf16.

@@ -115,9 +115,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) {
   if (tid < kPrepRows * half) {
     const int rr = tid / half;
     const int i = tid - rr * half;
-    float c, s;
-    rope_cos_sin(ppos[rr], a.rp.inv_freq[i], c, s);
-    csq[rr][i] = f32_to_bf16(c) | (f32_to_bf16(s) << 16);
+    csq[rr][i] = rope_cos_sin_bf16x2(ppos[rr], a.rp.inv_freq[i]);
   }
 
   // (1 + w) RMSNorm in double, rounded to f32 and then to bf16.

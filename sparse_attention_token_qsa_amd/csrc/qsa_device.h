@@ -117,10 +117,12 @@ __device__ __forceinline__ void cos_sin_small_angle(float angle, double& c, doub
 }
 
 // Rotary angle of position `p` at frequency `f`: one f32 product, then cos
-// and sin evaluated in double on that f32 angle and rounded to f32 and bf16.
-// Positions below 2^18 with frequencies at most 1 keep |angle| < 2^18; any
-// other angle goes through the library cos/sin.
-__device__ __forceinline__ void rope_cos_sin(int64_t p, float f, float& c, float& s) {
+// and sin evaluated in double on that f32 angle, rounded to f32 and then to
+// bf16.  Returned packed: cos in bits 0..15, sin in bits 16..31.  Positions
+// below 2^18 with frequencies at most 1 keep |angle| < 2^18; any other angle
+// goes through the library cos/sin.  Both values are finite (|.| <= 1), so the
+// hardware round-to-nearest-even conversion is the bf16 rounding.
+__device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int64_t p, float f) {
 #pragma clang fp contract(off)
   const float angle = static_cast<float>(p) * f;
   double sd, cd;
@@ -128,8 +130,12 @@ __device__ __forceinline__ void rope_cos_sin(int64_t p, float f, float& c, float
     cos_sin_small_angle(angle, cd, sd);
   else
     sincos(static_cast<double>(angle), &sd, &cd);
-  c = round_bf16(static_cast<float>(cd));
-  s = round_bf16(static_cast<float>(sd));
+  const float c = static_cast<float>(cd), s = static_cast<float>(sd);  // the f32 rounding first
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(c);
+  v[1] = static_cast<__bf16>(s);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Inverse RMS of a 128-channel vector from its sum of squares (double):

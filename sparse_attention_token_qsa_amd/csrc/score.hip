@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   const int half = rd >> 1;
   const int ncs = RG * half;
   for (int base = 0; base < ncs; base += 4 * kScoreThreads) {
-    float cv[4], sv[4];
+    uint32_t cs[4];
     int ri[4], fi[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -245,12 +245,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
       idx = idx < ncs ? idx : ncs - 1;
       ri[u] = idx / half;
       fi[u] = idx - ri[u] * half;
-      rope_cos_sin(ppos[ri[u]], a.rp.inv_freq[fi[u]], cv[u], sv[u]);
+      cs[u] = rope_cos_sin_bf16x2(ppos[ri[u]], a.rp.inv_freq[fi[u]]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (base + u * kScoreThreads + tid < ncs)
-        csq[ri[u]][fi[u]] = f32_to_bf16(cv[u]) | (f32_to_bf16(sv[u]) << 16);
+      if (base + u * kScoreThreads + tid < ncs) csq[ri[u]][fi[u]] = cs[u];
   }
 
   // ---- (1 + w) RMSNorm of every head vector this group holds
