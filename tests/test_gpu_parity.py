@@ -14,9 +14,10 @@ import torch
 
 import oracle as O
 import synth
+import sparse_attention_token_qsa_amd as qsa
 from tests.gpu_util import (DEV, gpu_pool, gpu_prep, gpu_scores, gpu_scores_prepped, gpu_select,
-                            gpu_select_indices, gpu_select_indices_ws, gpu_select_ws, note, u16_dev, u16_host,
-                            workload)
+                            gpu_select_indices, gpu_select_indices_ws, gpu_select_ws, i32_dev, note, status_word,
+                            u16_dev, u16_host, workload)
 from tests.test_oracle_pins import check_structure
 
 pytestmark = pytest.mark.gpu
@@ -428,10 +429,9 @@ def test_select_ws_equals_select_and_reuses_its_workspace():
     rows = 24
     pos = np.sort(rng.integers(T // 2, T, size=rows)).astype(np.int32)
     sc = rng.standard_normal((rows, cols)).astype(np.float32)
-    nbytes = __import__("sparse_attention_token_qsa_amd").qsa_select_workspace_bytes(rows, T)
+    nbytes = qsa.qsa_select_workspace_bytes(rows, T)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-    import sparse_attention_token_qsa_amd as qsa
-    from tests.gpu_util import f32_dev, i32_dev, status_word
+    from tests.gpu_util import f32_dev
     for p2 in (pos, pos // 3):
         mask = torch.full((rows, T), 0xAB, dtype=torch.uint8, device=DEV)
         st = status_word()
@@ -557,6 +557,39 @@ def test_score_long_batches_ragged_rows_bad_positions_nan_key():
             worst = max(worst, float(np.max(np.abs(g.astype(np.float64) - s))))
     note(f"  max |gpu - oracle| = {worst:.3e}")
     assert worst <= SCORE_ATOL
+
+
+def test_score_full_prefill_chunk_ring_equals_one_call_scorer():
+    """Every score of the 8192-row prefill chunk over 64k (125.8 M pairs, the
+    benchmarked launch: 128-row ring scorer, steady-state steps on interior
+    tiles) equals the one-call scorer's bit for bit (a different kernel: 32
+    rows per workgroup, queries normed and roped in its prologue), and the
+    columns past each row's prefix keep their sentinel.  Compared on the
+    device."""
+    w = workload(5)
+    T = w["tokens"]
+    rows = len(w["pos"])
+    cols = T // 4
+    note(f"score full chunk: {rows} rows over {T} tokens, ring vs one-call scorer")
+    pooled = gpu_pool(w)
+    pos = i32_dev(w["pos"])
+    qhat, s0 = gpu_prep(w)
+    assert s0 == 0
+    a = torch.full((rows * cols,), -7.25, dtype=torch.float32, device=DEV)
+    b = torch.full((rows * cols,), -7.25, dtype=torch.float32, device=DEV)
+    st = status_word()
+    qsa.qsa_score_prepped(qhat, pos, pooled, T, a, cols, st)
+    qsa.qsa_score_rows(u16_dev(w["queries"].reshape(rows, 512)), pos, u16_dev(w["q_norm_w"]), w["rotary_dim"],
+                       w["theta"], w["eps"], pooled, T, b, cols, st)
+    assert qsa.check_status(st) == 0
+    same = torch.equal(a.view(torch.int32), b.view(torch.int32))
+    if not same:
+        bad = torch.nonzero((a.view(torch.int32) != b.view(torch.int32)).view(rows, cols).any(dim=1)).flatten()
+        raise AssertionError(f"ring and one-call scores differ in rows {bad[:8].tolist()}")
+    n = (torch.from_numpy(w["pos"]).to(DEV).to(torch.int64) + 1) // 4
+    col = torch.arange(cols, device=DEV)
+    outside = col[None, :] >= n[:, None]
+    assert bool((a.view(rows, cols)[outside] == -7.25).all())
 
 
 # ------------------------------------------------------------ end to end ----
