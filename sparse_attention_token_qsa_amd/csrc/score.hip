@@ -808,49 +808,23 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
 
   int stage = 0, step = 0;
   int prev_nb0 = blk_begin;
-  // Step prologue: the next tile's loads, then this stage's B fragments.
-  auto begin_step = [&](int nb0, bf16x8_t (&bf)[8]) {
+  for (int nb0 = blk_begin; nb0 < nmax; nb0 += stride) {
     int lstage = stage + D - 1;
     lstage = lstage >= D ? lstage - D : lstage;
     load_tile(nb0 + (D - 1) * stride, lstage);
-    const uint32_t bb = bbase + stage * STAGE;
-    const uint32_t b0 = bb + s2x, b1 = bb + (32u ^ s2x), b2 = bb + (64u ^ s2x), b3 = bb + (96u ^ s2x);
-    bf[0] = lds_read16<0>(b0);
-    bf[1] = lds_read16<0>(b1);
-    bf[2] = lds_read16<0>(b2);
-    bf[3] = lds_read16<0>(b3);
-    bf[4] = lds_read16<128>(b0);
-    bf[5] = lds_read16<128>(b1);
-    bf[6] = lds_read16<128>(b2);
-    bf[7] = lds_read16<128>(b3);
-  };
-  auto mfma_pair = [&](int ms, const bf16x8_t (&bf)[8]) {
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms][ks], bf[ks], ks ? acc[ms] : f32x16_t{}, 0, 0, 0);
-      acc[ms + 1] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms + 1][ks], bf[ks], ks ? acc[ms + 1] : f32x16_t{}, 0, 0, 0);
-    }
-  };
-  // Tile t + 1 has landed once at most N of this wave's memory operations
-  // are outstanding, N = what was issued after its loads: the loads of
-  // (D - 2) tiles and the stores of each step since (D - 1 steps in the
-  // steady state, step + 1 in the first D - 2 steps).  Smaller N is safe.
-  // Every step issues kStores stores, whatever its epilogues keep.
-  constexpr int NA0 = (D - 2) * kL + (D - 1) * kStores;
-  constexpr int NA = NA0 > 63 ? 63 : NA0;
-  auto end_step = [&](int nb0) {
-    __builtin_amdgcn_s_barrier();  // the stage read this step may be refilled
-    asm volatile("" ::: "memory");
-    prev_nb0 = nb0;
-    ++step;
-    stage = stage + 1 == D ? 0 : stage + 1;
-  };
-  // Any step of the store mode: ragged tiles (rows that see only part of
-  // them) and the first D - 2 steps (ramp-up waits).
-  auto general_step = [&](int nb0) {
     bf16x8_t bf[8];
-    begin_step(nb0, bf);
+    {
+      const uint32_t bb = bbase + stage * STAGE;
+      const uint32_t b0 = bb + s2x, b1 = bb + (32u ^ s2x), b2 = bb + (64u ^ s2x), b3 = bb + (96u ^ s2x);
+      bf[0] = lds_read16<0>(b0);
+      bf[1] = lds_read16<0>(b1);
+      bf[2] = lds_read16<0>(b2);
+      bf[3] = lds_read16<0>(b3);
+      bf[4] = lds_read16<128>(b0);
+      bf[5] = lds_read16<128>(b1);
+      bf[6] = lds_read16<128>(b2);
+      bf[7] = lds_read16<128>(b3);
+    }
     // phase A: the previous step's acc[2..3] (dropped in the first step)
     epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin);
     lds_wait8(bf);
@@ -866,7 +840,14 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
     }
     epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin);
+    // Tile t + 1 has landed once at most N of this wave's memory operations
+    // are outstanding, N = what was issued after its loads: the loads of
+    // (D - 2) tiles and the stores of each step since (D - 1 steps in the
+    // steady state, step + 1 in the first D - 2 steps).  Smaller N is safe.
+    // Both epilogues issue kStores stores per step, whatever they keep.
     {
+      constexpr int NA0 = (D - 2) * kL + (D - 1) * kStores;
+      constexpr int NA = NA0 > 63 ? 63 : NA0;
       constexpr int N0 = (D - 2) * kL + kStores;
       constexpr int N1 = (D - 2) * kL + 2 * kStores;
       constexpr int N2 = (D - 2) * kL + 3 * kStores;
@@ -876,104 +857,11 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       else if (step == 1) wait_vmcnt<(N1 > 63 ? 63 : N1)>();
       else wait_vmcnt<(N2 > 63 ? 63 : N2)>();
     }
-    end_step(nb0);
-  };
-  if constexpr (EMIT) {
-    // The emit epilogue's own loop, written out: through general_step the
-    // compiler spills in emit mode.
-    for (int nb0 = blk_begin; nb0 < nmax; nb0 += stride) {
-      int lstage = stage + D - 1;
-      lstage = lstage >= D ? lstage - D : lstage;
-      load_tile(nb0 + (D - 1) * stride, lstage);
-      bf16x8_t bf[8];
-      {
-        const uint32_t bb = bbase + stage * STAGE;
-        const uint32_t b0 = bb + s2x, b1 = bb + (32u ^ s2x), b2 = bb + (64u ^ s2x), b3 = bb + (96u ^ s2x);
-        bf[0] = lds_read16<0>(b0);
-        bf[1] = lds_read16<0>(b1);
-        bf[2] = lds_read16<0>(b2);
-        bf[3] = lds_read16<0>(b3);
-        bf[4] = lds_read16<128>(b0);
-        bf[5] = lds_read16<128>(b1);
-        bf[6] = lds_read16<128>(b2);
-        bf[7] = lds_read16<128>(b3);
-      }
-      // phase A: the previous step's acc[2..3] (dropped in the first step)
-      epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin);
-      lds_wait8(bf);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[0][ks], bf[ks], ks ? acc[0] : f32x16_t{}, 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[1][ks], bf[ks], ks ? acc[1] : f32x16_t{}, 0, 0, 0);
-      }
-      // phase B: this step's acc[0..1]
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
-      }
-      epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin);
-      // Tile t + 1 has landed once at most N of this wave's memory operations
-      // are outstanding, N = what was issued after its loads: the loads of
-      // (D - 2) tiles and the stores of each step since (D - 1 steps in the
-      // steady state, step + 1 in the first D - 2 steps).  Smaller N is safe.
-      // Both epilogues issue kStores stores per step, whatever they keep.
-      {
-        constexpr int NA0 = (D - 2) * kL + (D - 1) * kStores;
-        constexpr int NA = NA0 > 63 ? 63 : NA0;
-        constexpr int N0 = (D - 2) * kL + kStores;
-        constexpr int N1 = (D - 2) * kL + 2 * kStores;
-        constexpr int N2 = (D - 2) * kL + 3 * kStores;
-        static_assert(D <= 5, "steps before the steady state: at most three");
-        if (step >= D - 2) wait_vmcnt<NA>();
-        else if (step == 0) wait_vmcnt<(N0 > 63 ? 63 : N0)>();
-        else if (step == 1) wait_vmcnt<(N1 > 63 ? 63 : N1)>();
-        else wait_vmcnt<(N2 > 63 ? 63 : N2)>();
-      }
-      __builtin_amdgcn_s_barrier();  // the stage read this step may be refilled
-      asm volatile("" ::: "memory");
-      prev_nb0 = nb0;
-      ++step;
-      stage = stage + 1 == D ? 0 : stage + 1;
-    }
-  } else {
-    int nb0 = blk_begin;
-    for (; nb0 < nmax && step < D - 2; nb0 += stride) general_step(nb0);
-    // Steady state over interior tiles (every row of the group sees both
-    // phases' blocks): one branch-free block per step, so the scheduler can
-    // thread each phase's score VALU and stores between the MFMAs of the
-    // other accumulator pair (one MFMA, five VALU, and a store every second
-    // MFMA), instead of leaving them to the other wave on the SIMD.
-    for (; nb0 + TILE <= nmin; nb0 += stride) {
-      bf16x8_t bf[8];
-      begin_step(nb0, bf);
-      lds_wait8(bf);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)  // phase A: acc[2..3] of the previous step
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pair_score(acc[2 + (j >> 2)], j & 3)), orsrc, vbase,
-                                              (8 * (2 + (j >> 2)) + 2 * (j & 3)) * rowbytes + 4 * prev_nb0, 0);
-      mfma_pair(0, bf);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);  // memory write
-      }
-      mfma_pair(2, bf);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)  // phase B: this step's acc[0..1]
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pair_score(acc[j >> 2], j & 3)), orsrc, vbase,
-                                              (8 * (j >> 2) + 2 * (j & 3)) * rowbytes + 4 * nb0, 0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
-      }
-      wait_vmcnt<NA>();
-      end_step(nb0);
-    }
-    for (; nb0 < nmax; nb0 += stride) general_step(nb0);
+    __builtin_amdgcn_s_barrier();  // the stage read this step may be refilled
+    asm volatile("" ::: "memory");
+    prev_nb0 = nb0;
+    ++step;
+    stage = stage + 1 == D ? 0 : stage + 1;
   }
   epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, true, prev_nb0 + TILE <= nmin);
   if constexpr (EMIT) store_counts();
