@@ -336,6 +336,19 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
     return;
   }
   const int n = static_cast<int>((p + 1) / kRatio);
+  // The union's slots, loaded before the counts arrive: every chunk before
+  // the row's last visible one is full (4096 >= keep blocks) and emitted
+  // exactly keep composites, so slot i is entry i % keep of chunk i / keep;
+  // slots past the emitted total are cleared once the counts are known.
+  const int keep = a.keep_max;
+  const uint64_t* base = a.cand + row * a.chunks * kMaxKeep;
+  uint64_t cv[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = tid + j * NT;
+    const int c = i / keep;
+    cv[j] = c < a.chunks ? base[static_cast<int64_t>(c) * kMaxKeep + (i - c * keep)] : 0ull;
+  }
   if (tid < a.chunks) cnts[tid] = a.cnt[row * a.chunks + tid];
   if (tid < 64) kcount[tid] = 0;
   if (tid < kSplitChunk / 32) keptbits[tid] = 0u;
@@ -361,20 +374,10 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
     write_slice(0, p, false);
     return;
   }
-  const int keep = a.keep_max;
 
-  // the union, KPT composites per thread (0 = absent).  Every chunk before
-  // the row's last visible one is full (4096 >= keep blocks) and emitted
-  // exactly keep composites, so candidate i is entry i % keep of chunk
-  // i / keep.
-  const uint64_t* base = a.cand + row * a.chunks * kMaxKeep;
-  uint64_t cv[KPT];
+  // the union, KPT composites per thread (0 = absent)
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = tid + j * NT;
-    const int c = i / keep;
-    cv[j] = i < total ? base[static_cast<int64_t>(c) * kMaxKeep + (i - c * keep)] : 0ull;
-  }
+  for (int j = 0; j < KPT; ++j) cv[j] = tid + j * NT < total ? cv[j] : 0ull;
   // prefilter: the wave's r-th largest thread maximum, minimum over waves
   uint32_t t1 = 0u;
 #pragma unroll
