@@ -475,7 +475,10 @@ def decode_next(d: Device, torch, qsa):
     g_cold = cold_launch_us(gather, torch)
     if qsa.check_status(d.status) != 0:
         raise RuntimeError("device status set in the decode gather")
-    graph_fig = decode_graph(d, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab)
+    n_sel_pre = int(counts.sum().item())
+    gather_bytes = (4 * KV_DIM * n_sel_pre + 4 * KV_DIM * d.rows * slots
+                    + 4 * d.rows * (stride + 1 + slots // PAGE_SIZE))
+    graph_fig = decode_graph(d, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab, gather_bytes)
     n_sel = int(counts.sum().item())
     alg = 4 * KV_DIM * n_sel + 4 * KV_DIM * d.rows * slots + 4 * d.rows * (stride + 1 + slots // PAGE_SIZE)
     gbs = alg / (g_us * 1e-6) / 1e9
@@ -494,12 +497,15 @@ def decode_next(d: Device, torch, qsa):
             "decode_step": graph_fig}
 
 
-def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab):
+def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab, gather_bytes):
     """One production decode step with the cache length in a device word:
     pool the block the new token completed, prep, score, index-list select,
     K/V gather.  Timed as eager launches and as one captured HIP graph
     replayed back to back (positions and cache fixed; each replay redoes the
-    same step)."""
+    same step), and cold (caches flushed before each step, one event pair
+    around it), with the step's algorithmic bytes: one pooled block, the
+    queries, the score stage's bytes, the scores read and index lists
+    written by the select, and the gather's bytes."""
     w = d.w
     rd, th, eps = w["rotary_dim"], w["theta"], w["eps"]
     dt = torch.full((1,), d.T, dtype=torch.int32, device="cuda:0")
@@ -512,6 +518,10 @@ def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko,
         qsa.qsa_gather_kv(kc, vc, table, 0, n_pages, idx, counts, ko, vo, otab, d.status)
 
     eager_us = launch_us(step, torch)
+    cold_us = cold_launch_us(step, torch)
+    stride = idx.shape[1]
+    alg = (4 * 256 + 256 + d.prep_bytes() + d.score_bytes() + 4 * d.pairs
+           + d.rows * (4 * stride + 4) + gather_bytes)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -527,7 +537,9 @@ def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko,
         raise RuntimeError("device status set in the captured decode step")
     del graph
     return {"stages": "pool_window(1 block) + prep + score + select_indices + gather",
-            "eager_us": eager_us, "graph_replay_us": replay_us}
+            "eager_us": eager_us, "graph_replay_us": replay_us, "cold_us": cold_us, "alg_bytes": alg,
+            "hbm_frac_eager": round(alg / (eager_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "hbm_frac_cold": round(alg / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def fused_prefill(d: Device, torch, qsa):
