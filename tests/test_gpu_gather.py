@@ -87,6 +87,16 @@ def test_gather_elementwise_path(kv_dim, offset):
     assert check(kc, vc, table, ts, 40, idx, counts, 104, offset=offset, label="element-wise") == 0
 
 
+@pytest.mark.parametrize("per_row", [False, True])
+def test_gather_bit_exact_large_batch(per_row):
+    """A batch of 40 rows x 2064 entries (at least 65536 entries: the form
+    that moves two entries per wave), random counts up to the whole list,
+    against the oracle."""
+    rng = np.random.default_rng(35)
+    kc, vc, table, ts, idx, counts = random_case(rng, 40, 300, 11, 16, 64, 2051, per_row)
+    assert check(kc, vc, table, ts, 300, idx, counts, 2064, label="large batch") == 0
+
+
 def test_gather_bad_indices_and_counts():
     rng = np.random.default_rng(33)
     kc, vc, table, ts, idx, counts = random_case(rng, 4, 30, 2, 16, 64, 64)
