@@ -595,12 +595,13 @@ def fused_prefill(d: Device, torch, qsa):
 
 
 def side_figures(torch, qsa, synth):
-    """select+mask us/row on the 64k/256k decode workloads and the one-row
-    64k/256k shapes: per-kernel event means over 20 launches after 5 warm-ups
+    """The 4096-row prefill over 4k tokens, select+mask us/row on the 64k/256k
+    decode workloads and the one-row 64k/256k shapes: per-kernel event means over 20 launches after 5 warm-ups
     (each launch between its own event pair), per-kernel back-to-back launch
     times, and the cold-cache step with its aggregate HBM fraction."""
     out = {}
-    for key, w in (("decode_64k_x64", synth.make_workload(3)),
+    for key, w in (("prefill_4k", synth.make_workload(2)),
+                   ("decode_64k_x64", synth.make_workload(3)),
                    ("decode_256k_x16", synth.make_workload(4)),
                    ("one_row_64k", synth.single_row(3, 65535)),
                    ("one_row_256k", synth.single_row(4, 262143))):
@@ -622,7 +623,8 @@ def side_figures(torch, qsa, synth):
                     "pairs_per_s": round(d.pairs / (sum(b2b.values()) * 1e-6), 1),
                     "kernels_back_to_back_us": b2b,
                     "kernels": rep}
-        out[key].update(decode_next(d, torch, qsa))
+        if key != "prefill_4k":  # decode consumers of the selection
+            out[key].update(decode_next(d, torch, qsa))
         del d
         torch.cuda.empty_cache()
     return out
