@@ -442,6 +442,34 @@ def test_select_ws_equals_select_and_reuses_its_workspace():
     assert qsa.qsa_select_workspace_bytes(4096, T) == 0
 
 
+@pytest.mark.parametrize("rows,T", [(1024, 4096), (2048, 65536), (3072, 8192)])
+def test_select_row_order_of_whole_row_groups(rows, T):
+    """Batches of a multiple of 1024 rows are visited in a group order, not
+    by row index: every row is written, and each equals the same row selected
+    in batches of other sizes (index order) and, on a sample, the oracle."""
+    from tests.gpu_util import f32_dev
+    note(f"select row order: {rows} rows over {T} tokens")
+    rng = np.random.default_rng(rows + T)
+    cols = T // 4
+    pos = rng.integers(0, T, size=rows).astype(np.int32)
+    sc = rng.standard_normal((rows, cols)).astype(np.float32)
+    budget = 2048
+    mask = torch.full((rows, T), 0xAB, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    qsa.qsa_select_mask(f32_dev(sc.reshape(-1)), cols, i32_dev(pos), T, budget, mask, st)
+    assert qsa.check_status(st) == 0
+    got = mask.cpu().numpy()
+    assert got.max() <= 1  # no row left unwritten
+    cut = 1000
+    head, hst = gpu_select(sc[:cut], cols, pos[:cut], T, budget)
+    tail, tst = gpu_select(sc[cut:], cols, pos[cut:], T, budget)
+    assert hst == 0 and tst == 0
+    assert np.array_equal(got[:cut], head) and np.array_equal(got[cut:], tail)
+    sample = np.sort(rng.choice(rows, 12, replace=False))
+    want, wst = O.select_mask(sc[sample], cols, pos[sample], T, budget)
+    assert wst == 0 and np.array_equal(got[sample], want)
+
+
 # ----------------------------------------------------------------- score ----
 
 @pytest.mark.parametrize("path", ["fused", "prepped"])
