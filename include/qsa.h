@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 7
+#define QSA_ABI_VERSION 8
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -286,6 +286,17 @@ int qsa_score_select_mask(const uint16_t* qhat, const int32_t* pos, int64_t rows
                           const uint16_t* pooled, int64_t tokens, int64_t budget, uint8_t* mask,
                           int32_t* dev_status, void* workspace, int64_t workspace_bytes,
                           void* stream);
+
+/*
+ * qsa_score_select_flags_offset -- where qsa_score_select_mask records which
+ * rows it selected in full: the byte offset, within its workspace, of an
+ * int32 [rows] array that a call leaves holding 1 for every row whose
+ * sampled threshold did not settle it (scored and selected in full inside
+ * the call) and 0 for every other row.  The mask does not depend on it; it
+ * tells tests and tuning which path each row took.  0 for an empty call;
+ * negative QSA_ERR_* as qsa_score_select_workspace_bytes.
+ */
+int64_t qsa_score_select_flags_offset(int64_t rows, int64_t tokens, int64_t budget);
 
 /*
  * qsa_gather_kv -- each row's selected tokens' K and V vectors, copied from a

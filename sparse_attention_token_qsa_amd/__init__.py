@@ -21,7 +21,8 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
-           "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_mask",
+           "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_flags_offset",
+           "qsa_score_select_mask",
            "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
            "qsa_select_indices_dev", "qsa_select_indices_ws",
            "qsa_rope_inv_freq",
@@ -239,6 +240,15 @@ def qsa_score_select_workspace_bytes(rows: int, tokens: int, budget: int) -> int
     n = load().qsa_score_select_workspace_bytes(rows, tokens, budget)
     if n < 0:
         raise QsaError(int(n), "qsa_score_select_workspace_bytes")
+    return int(n)
+
+
+def qsa_score_select_flags_offset(rows: int, tokens: int, budget: int) -> int:
+    """Byte offset, in qsa_score_select_mask's workspace, of the int32 [rows]
+    flags that mark the rows the call selected in full."""
+    n = load().qsa_score_select_flags_offset(rows, tokens, budget)
+    if n < 0:
+        raise QsaError(int(n), "qsa_score_select_flags_offset")
     return int(n)
 
 

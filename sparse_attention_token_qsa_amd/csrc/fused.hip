@@ -15,12 +15,9 @@
 //    an unsigned integer), r = max(ceil(2.5 keep / 16), 32): about 2.5 keep
 //    blocks of the row score at least T.  Rows under the budget take T =
 //    +Inf (only non-finite scores are of interest there); rows with fewer
-//    than r samples take T = 0 (every block).  The scorer compares head sums
-//    (the score before its final scale), so T is mapped to U, the least sum
-//    whose scaled score reaches T: sum >= U exactly when score >= T, and
-//    every sum below U scores strictly below T.
+//    than r samples take T = 0 (every block).
 // 3. Emit pass.  The ring scorer scores every block but stores only the
-//    (sum bits, block) pairs with sum >= U, in fixed-capacity regions per
+//    (score bits, block) pairs with score >= T, in fixed-capacity regions per
 //    (row, workgroup split, 8-block column group), with exact per-region
 //    counts.
 // 4. Candidate select, one workgroup per row.  If any stored candidate is
@@ -114,25 +111,6 @@ struct ThrArgs {
   int32_t* gflag;
 };
 
-// U for a score threshold T (bits): the least head sum u >= 0 with
-// fl(u * 0.5 / sqrt(128)) >= T.  The scaled score is a non-decreasing
-// function of the sum, so {sum >= U} = {score >= T}, and a sum below U scores
-// below T.  +Inf and above map to +Inf: non-finite sums only.
-__device__ uint32_t sum_threshold(uint32_t t) {
-  if (t == 0xFFFFFFFFu) return t;  // no visible block
-  if (t >= 0x7F800000u) return 0x7F800000u;
-  if (t == 0u) return 0u;
-  const float c = 0.5f * kScale;
-  const float T = __uint_as_float(t);
-  uint32_t u = __float_as_uint(T / c);
-  if (u > 0x7F800000u) u = 0x7F800000u;
-  for (int i = 0; i < 64 && !(__uint_as_float(u) * c >= T); ++i) ++u;
-  for (int i = 0; i < 64 && u > 0u && __uint_as_float(u - 1u) * c >= T; ++i) --u;
-  // not settled (never expected): 0 keeps every block, still exact
-  const bool least = __uint_as_float(u) * c >= T && (u == 0u || !(__uint_as_float(u - 1u) * c >= T));
-  return least ? u : 0u;
-}
-
 // One wave per row; KPL sampled scores per lane (KPL * 64 >= the row's).
 template <int KPL>
 __global__ __launch_bounds__(256) void threshold_kernel(const ThrArgs a) {
@@ -184,7 +162,7 @@ __global__ __launch_bounds__(256) void threshold_kernel(const ThrArgs a) {
       }
     }
   }
-  if (lane == 0) a.thr[row] = sum_threshold(t < 0x7F800000u || t == 0xFFFFFFFFu ? t : 0x7F800000u);
+  if (lane == 0) a.thr[row] = t < 0x7F800000u || t == 0xFFFFFFFFu ? t : 0x7F800000u;
 }
 
 // ---- 4. candidate select and mask ----
@@ -273,7 +251,6 @@ __global__ __launch_bounds__(256) void cand_select_kernel(const CandArgs a) {
   }
   __syncthreads();
   // the candidates as composites, KPT per thread (0 = absent; keys are >= 2^31)
-  const float scale = 0.5f * kScale;
   const uint2* rbase = a.cand + row * S * a.cap;
   uint64_t cv[KPT];
   bool nonfin = false;
@@ -285,7 +262,7 @@ __global__ __launch_bounds__(256) void cand_select_kernel(const CandArgs a) {
       const int s = owner[i];
       const uint2 e = rbase[static_cast<int64_t>(s) * a.cap + (i - offs[s])];
       nonfin |= (e.x & 0x7F800000u) == 0x7F800000u;
-      cv[j] = composite(score_key(__uint_as_float(e.x) * scale), static_cast<int>(e.y));
+      cv[j] = composite(score_key(__uint_as_float(e.x)), static_cast<int>(e.y));
     }
   }
   if (__syncthreads_or(nonfin ? 1 : 0)) {
@@ -373,6 +350,10 @@ __global__ __launch_bounds__(256) void cand_select_kernel(const CandArgs a) {
 
 int64_t score_select_workspace_bytes(int64_t rows, int64_t tokens, int keep_max) {
   return layout(rows, tokens, keep_max).total;
+}
+
+int64_t score_select_flags_offset(int64_t rows, int64_t tokens, int keep_max) {
+  return layout(rows, tokens, keep_max).off_rflag;
 }
 
 hipError_t launch_score_select(const uint16_t* qhat, const int32_t* pos, int64_t rows,

@@ -55,23 +55,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Sum over the 16 lanes of a DPP row, returned in all 16.  Used on sums of
-// squares of bf16 values, exact in double in any order.
-__device__ __forceinline__ double row16_sum(double v) {
-#define QSA_ROR_STEP(CTRL)                                                                  \
-  {                                                                                         \
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false); \
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false); \
-    v += __hiloint2double(hi, lo);                                                          \
-  }
-  QSA_ROR_STEP(0x128)  // row_ror 8
-  QSA_ROR_STEP(0x124)  // row_ror 4
-  QSA_ROR_STEP(0x122)  // row_ror 2
-  QSA_ROR_STEP(0x121)  // row_ror 1
-#undef QSA_ROR_STEP
-  return v;
-}
-
 template <bool kVec>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t csq[kPoolBlocksPerGroup][kMaxHalfRotary];

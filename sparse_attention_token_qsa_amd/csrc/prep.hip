@@ -35,24 +35,6 @@ struct PrepArgs {
   RopeParams rp;
 };
 
-// Sum over the 16 lanes of a DPP row, returned in all 16 (rotations 8, 4, 2,
-// 1).  Used on sums of squares of bf16 values, which are exact in double in
-// any order, so every lane gets the same value.
-__device__ __forceinline__ double row16_sum(double v) {
-#define QSA_ROR_STEP(CTRL)                                                                  \
-  {                                                                                         \
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false); \
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false); \
-    v += __hiloint2double(hi, lo);                                                          \
-  }
-  QSA_ROR_STEP(0x128)  // row_ror 8
-  QSA_ROR_STEP(0x124)  // row_ror 4
-  QSA_ROR_STEP(0x122)  // row_ror 2
-  QSA_ROR_STEP(0x121)  // row_ror 1
-#undef QSA_ROR_STEP
-  return v;
-}
-
 __device__ __forceinline__ void unpack8(const uint4 u, float (&v)[8]) {
   const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll

@@ -233,6 +233,12 @@ int64_t qsa_score_select_workspace_bytes(int64_t rows, int64_t tokens, int64_t b
   return qsa::score_select_workspace_bytes(rows, tokens, static_cast<int>(budget / QSA_RATIO));
 }
 
+int64_t qsa_score_select_flags_offset(int64_t rows, int64_t tokens, int64_t budget) {
+  const int64_t n = qsa_score_select_workspace_bytes(rows, tokens, budget);
+  if (n <= 0) return n;
+  return qsa::score_select_flags_offset(rows, tokens, static_cast<int>(budget / QSA_RATIO));
+}
+
 int qsa_score_select_mask(const uint16_t* qhat, const int32_t* pos, int64_t rows,
                           const uint16_t* pooled, int64_t tokens, int64_t budget, uint8_t* mask,
                           int32_t* dev_status, void* workspace, int64_t workspace_bytes,

@@ -26,6 +26,38 @@ __device__ __forceinline__ int64_t live_tokens(int64_t ceiling, const int32_t* d
 // score scale 1/sqrt(head dim), rounded once to f32
 constexpr float kScale = static_cast<float>(0.088388347648318440550);
 
+// Score of one (row, block) pair from its four head dot products: relu per
+// head as a comparison (d < 0 ? 0 : d, so NaN stays NaN and -Inf gives 0),
+// heads summed in order in f32, then the 1/sqrt(128) scale.
+__device__ __forceinline__ float score_exact(float h0, float h1, float h2, float h3) {
+#pragma clang fp contract(off)
+  const float r0 = h0 < 0.0f ? 0.0f : h0;
+  const float r1 = h1 < 0.0f ? 0.0f : h1;
+  const float r2 = h2 < 0.0f ? 0.0f : h2;
+  const float r3 = h3 < 0.0f ? 0.0f : h3;
+  float s = r0 + r1;
+  s = s + r2;
+  s = s + r3;
+  return s * kScale;
+}
+
+// The same score in fewer instructions: relu(d) = (d + |d|) / 2, so the head
+// sum of the doubled terms, times scale / 2, is the score: doubling commutes
+// with every f32 rounding of the sum.  Equal to score_exact whenever the
+// result is finite; it differs only where a doubled term or sum overflows or
+// a head is -Inf (then -Inf + Inf = NaN), and then the result is +Inf or NaN.
+// Callers recompute a non-finite result with score_exact.  A -0.0 head term
+// becomes +0.0, which only changes the sign of an all-zero score.  The
+// result is >= +0 or NaN, so its bits as an unsigned integer reach
+// 0x7F800000 exactly when it is not finite.
+__device__ __forceinline__ float score_fast(float h0, float h1, float h2, float h3) {
+#pragma clang fp contract(off)
+  float s = (h0 + fabsf(h0)) + (h1 + fabsf(h1));
+  s = s + (h2 + fabsf(h2));
+  s = s + (h3 + fabsf(h3));
+  return s * (0.5f * kScale);
+}
+
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -136,6 +168,30 @@ __device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int64_t p, float f) {
   v[0] = static_cast<__bf16>(c);
   v[1] = static_cast<__bf16>(s);
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Sum over the 16 lanes of a DPP row, returned in all 16 (rotations 8, 4, 2,
+// 1).  Used on the sums of squares of bf16 values behind the RMSNorm: each
+// square has at most 16 significant bits, so a double sum of 128 of them is
+// exact, and the same in any order, while the vector's channel magnitudes
+// span less than about 2^18 (the smallest square's lowest bit then stays
+// above the sum's last place).  A wider span rounds the sum in an order
+// that may differ from another implementation's by one double ulp, which
+// reaches a bf16 output only through a value within about 2^-52 of an f32
+// rounding boundary.
+__device__ __forceinline__ double row16_sum(double v) {
+#define QSA_ROR_STEP(CTRL)                                                                  \
+  {                                                                                         \
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false); \
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false); \
+    v += __hiloint2double(hi, lo);                                                          \
+  }
+  QSA_ROR_STEP(0x128)  // row_ror 8
+  QSA_ROR_STEP(0x124)  // row_ror 4
+  QSA_ROR_STEP(0x122)  // row_ror 2
+  QSA_ROR_STEP(0x121)  // row_ror 1
+#undef QSA_ROR_STEP
+  return v;
 }
 
 // Inverse RMS of a 128-channel vector from its sum of squares (double):

@@ -70,8 +70,8 @@ hipError_t launch_select_flagged(const float* scores, int64_t score_cols, const 
 // pooled keys streamed through LDS.  Column j of a row scores the pooled key
 // of block j * bstride; row r has ceil(((pos[r] + 1) / 4) / bstride) columns.
 // With cand == NULL the scores go to scores[r * score_cols + j].  Otherwise
-// nothing is stored but the blocks whose head sum (the score before its final
-// scale 0.5 / sqrt(128)) has bits >= thr[r], as (sum bits, block) entries in
+// nothing is stored but the blocks whose score has bits >= thr[r] (as
+// unsigned integers), as (score bits, block) entries in
 // cand[((r * splits + split) * 4 + g) * cap + e], e < cap, where g = (block
 // % 32) / 8, with the per-region totals in cnt[(r * splits + split) * 4 + g].
 // group_flag, when set, restricts the job to row groups whose flag is nonzero.
@@ -105,6 +105,8 @@ hipError_t launch_gather_kv(const uint16_t* k, const uint16_t* v, int64_t n_page
 
 // Fused score -> select for prefill batches (fused.hip).
 int64_t score_select_workspace_bytes(int64_t rows, int64_t tokens, int keep_max);
+// byte offset of the per-row fallback flags (int32 [rows]) in that workspace
+int64_t score_select_flags_offset(int64_t rows, int64_t tokens, int keep_max);
 hipError_t launch_score_select(const uint16_t* qhat, const int32_t* pos, int64_t rows,
                                const uint16_t* pooled, int64_t tokens, int keep_max,
                                uint8_t* mask, int32_t* status, void* workspace,

@@ -73,24 +73,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Waits until this wave's LDS operations have completed.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (3 << 14)); }
 
-// Sum over the 16 lanes of a DPP row, returned in all 16 (rotations 8, 4, 2,
-// 1).  Used on sums of squares of bf16 values, which are exact in double in
-// any order, so every lane gets the same value.
-__device__ __forceinline__ double row16_sum(double v) {
-#define QSA_ROR_STEP(CTRL)                                                                  \
-  {                                                                                         \
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false); \
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false); \
-    v += __hiloint2double(hi, lo);                                                          \
-  }
-  QSA_ROR_STEP(0x128)  // row_ror 8
-  QSA_ROR_STEP(0x124)  // row_ror 4
-  QSA_ROR_STEP(0x122)  // row_ror 2
-  QSA_ROR_STEP(0x121)  // row_ror 1
-#undef QSA_ROR_STEP
-  return v;
-}
-
 __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
   uint4 o;
   o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
@@ -408,22 +390,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
       for (int ms = 0; ms < MS; ++ms)
         acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms][ks], b, acc[ms], 0, 0, 0);
     }
-    // relu(d) = (d + |d|) / 2 exactly (0 or d; NaN stays NaN), so the head
-    // sum of the doubled terms is exactly twice the sum of the relu terms and
-    // one multiply by scale / 2 gives the same f32 score.  A -0.0 head term
-    // becomes +0.0, which only changes the sign of an all-zero score.
+    // relu -> head sum -> scale through the doubled terms (score_fast); a
+    // non-finite result, rare, is recomputed exactly.
     float sc[MS][4];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
+    for (int ms = 0; ms < MS; ++ms) {
+      uint32_t top = 0u;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float h0 = acc[ms][4 * q4 + 0], h1 = acc[ms][4 * q4 + 1];
-        const float h2 = acc[ms][4 * q4 + 2], h3 = acc[ms][4 * q4 + 3];
-        float s = (h0 + fabsf(h0)) + (h1 + fabsf(h1));
-        s = s + (h2 + fabsf(h2));
-        s = s + (h3 + fabsf(h3));
-        sc[ms][q4] = s * (0.5f * kScale);
+        sc[ms][q4] = score_fast(acc[ms][4 * q4 + 0], acc[ms][4 * q4 + 1], acc[ms][4 * q4 + 2],
+                                acc[ms][4 * q4 + 3]);
+        top = max(top, __float_as_uint(sc[ms][q4]));
       }
+      if (top >= 0x7F800000u) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          sc[ms][q4] = score_exact(acc[ms][4 * q4 + 0], acc[ms][4 * q4 + 1], acc[ms][4 * q4 + 2],
+                                   acc[ms][4 * q4 + 3]);
+      }
+    }
     const int blk = nb0 + col;
     if (nb0 + TILE <= nmin) {  // every lane's block is inside its row's prefix
 #pragma unroll
@@ -511,8 +496,8 @@ struct RingArgs {
   int64_t score_cols;
   int32_t* status;              // may be null: bad positions are then not flagged
   const int32_t* group_flag;    // non-null: only row groups with a nonzero flag run
-  const uint32_t* thr;          // EMIT: per-row thresholds (head-sum bits), 128-row padded
-  uint2* cand;                  // EMIT: [rows][splits][4][cap] (sum bits, block)
+  const uint32_t* thr;          // EMIT: per-row thresholds (score bits), 128-row padded
+  uint2* cand;                  // EMIT: [rows][splits][4][cap] (score bits, block)
   int32_t* cnt;                 // EMIT: [rows][splits][4] blocks at or above the threshold
   int cap;
   int splits;  // workgroups per row group; split s takes tiles s, s + splits, ...
@@ -550,34 +535,18 @@ __device__ __forceinline__ int lds_read_word(uint32_t addr) {
   return v;
 }
 
-// Score of query row (q4 of the lane's accumulator rows) from its four head
-// dot products: relu(d) = (d + |d|) / 2 exactly (NaN stays NaN), so the head
-// sum of the doubled terms times scale / 2 is the f32 score.
-// pair_sum is the head sum before the final scale: the score is exactly
-// pair_sum * (0.5 * scale) rounded once, a non-decreasing function of it.
-__device__ __forceinline__ float pair_sum(const f32x16_t& acc, int q4) {
-  const float h0 = acc[4 * q4 + 0], h1 = acc[4 * q4 + 1];
-  const float h2 = acc[4 * q4 + 2], h3 = acc[4 * q4 + 3];
-  float s = (h0 + fabsf(h0)) + (h1 + fabsf(h1));
-  s = s + (h2 + fabsf(h2));
-  s = s + (h3 + fabsf(h3));
-  return s;
-}
-__device__ __forceinline__ float pair_score(const f32x16_t& acc, int q4) {
-  return pair_sum(acc, q4) * (0.5f * kScale);
-}
-
-// EMIT: instead of storing the scores, the kernel keeps the blocks whose head
-// sum (pair_sum, the score before its final scale), read as an unsigned
-// integer, is at least the row's threshold thr[row] (given in the sum
-// domain).  Sums are never negative (relu terms), so this is their order, and
-// NaN / +-Inf bits lie above every threshold up to +Inf: non-finite scores are
-// always kept, for the selector to refuse.  Each epilogue phase (16 rows x 32
+// EMIT: instead of storing the scores, the kernel keeps the blocks whose
+// score, read as an unsigned integer, is at least the row's threshold
+// thr[row] (score bits).  Scores are +-0 or positive or NaN: for finite
+// thresholds this is their order (a -0.0 score, from an all -0.0 head set,
+// reads as large and is kept, which only adds a candidate), and NaN / +Inf
+// bits lie above every threshold up to +Inf: non-finite scores are always
+// kept, for the selector to refuse.  Each epilogue phase (16 rows x 32
 // blocks of a wave) goes through a small LDS tile so that lane l owns row
 // l / 4 of the phase and blocks 8 (l % 4) .. + 7 of the tile: its threshold
 // and its running count stay in the lane, and a kept block is one compare and
 // one store, with no cross-lane work.  Kept blocks go to the region of (row,
-// split, l % 4), cap entries of (sum bits, block); the counts, which may
+// split, l % 4), cap entries of (score bits, block); the counts, which may
 // exceed cap (the excess overwrote the region's last entry), finally go to
 // cnt[row][split][l % 4].
 template <int WM, bool EMIT>
@@ -689,9 +658,6 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
           row * kbytes + 16 * (lchunk ^ (row & 7)), nb0 * kbytes, 0, 0);
     }
   };
-#pragma unroll
-  for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t);
-
   // B fragment ks of lane (r, h): stage row 32 ng + r, logical chunk 2 ks + h
   // at chunk (2 ks + h) ^ (r & 7) = 2 ((ks & 3) ^ s2) + (h ^ s1) + 8 (ks >> 2).
   const int r = lane & 31, h = lane >> 5;
@@ -711,24 +677,41 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   const int rowbytes = EMIT ? 0 : static_cast<int>(a.score_cols) * 4;
   constexpr int kDrop = static_cast<int>(0x80000000u);
 
-  auto pair_store = [&](const f32x16_t& x0, const f32x16_t& x1, int m0, int nb0, bool live, bool fast) {
+  // Fast pass: scores through score_fast, and `seen` (a wave-uniform mask in
+  // scalar registers: the ring loop has no vector register to spare) records
+  // the lanes that produced a non-finite one; exact pass: score_exact (see
+  // the end).
+  uint64_t seen = 0u;
+  auto store_off = [&](int ms, int q4, int nb0, bool live, bool fast) {
+    if (fast) return vbase;
+    const int nv = lds_read_word(nvis_lane + 4 * (8 * ms + 2 * q4));
+    return (live && nb0 + col < nv) ? vbase : kDrop;
+  };
+  auto phase_score = [&](const f32x16_t& x, int q4, auto exact_c) {
+    if constexpr (decltype(exact_c)::value)
+      return score_exact(x[4 * q4 + 0], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+    else
+      return score_fast(x[4 * q4 + 0], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+  };
+  // the largest bits of a phase's eight fast scores into `seen`
+  auto note_phase = [&](const float (&sc)[8]) {
+    uint32_t t = max(max(__float_as_uint(sc[0]), __float_as_uint(sc[1])), __float_as_uint(sc[2]));
+    t = max(max(t, __float_as_uint(sc[3])), __float_as_uint(sc[4]));
+    t = max(max(t, __float_as_uint(sc[5])), __float_as_uint(sc[6]));
+    t = max(t, __float_as_uint(sc[7]));
+    seen |= __builtin_amdgcn_ballot_w64(t >= 0x7F800000u);
+  };
+  auto pair_store = [&](const f32x16_t& x0, const f32x16_t& x1, int m0, int nb0, bool live, bool fast,
+                        auto exact_c) {
     float sc[8];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      sc[q4] = pair_score(x0, q4);
-      sc[4 + q4] = pair_score(x1, q4);
-    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ms = m0 + (j >> 2), q4 = j & 3;
-      int off = vbase;
-      if (!fast) {
-        const int nv = lds_read_word(nvis_lane + 4 * (8 * ms + 2 * q4));
-        off = (live && nb0 + col < nv) ? vbase : kDrop;
-      }
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[j]), orsrc, off,
+      sc[j] = phase_score(j < 4 ? x0 : x1, q4, exact_c);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[j]), orsrc, store_off(ms, q4, nb0, live, fast),
                                             (8 * ms + 2 * q4) * rowbytes + 4 * nb0, 0);
     }
+    if constexpr (!decltype(exact_c)::value) note_phase(sc);
   };
 
   // EMIT: regions of the group's rows, [row][split][4][cap]
@@ -740,19 +723,27 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   const uint32_t etile_w = lds_addr(etile) + 4 * (wave * 16 * kEPitch);
   const uint32_t ewrite = etile_w + 4 * (h * kEPitch + r);        // lane (r, h) writes
   const uint32_t eread = etile_w + 4 * (er * kEPitch + 8 * cg);   // lane l reads
-  auto pair_emit = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast) {
+  auto pair_emit = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast,
+                       auto exact_c) {
     constexpr int m0 = decltype(m0c)::value;
-    // the phase's sums into the wave's tile: slot (ms, q4) of lane (r, h) is
-    // tile row 8 (ms - m0) + 2 q4 + h, column r
-    lds_write_word<4 * 0 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 0)));
-    lds_write_word<4 * 2 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 1)));
-    lds_write_word<4 * 4 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 2)));
-    lds_write_word<4 * 6 * kEPitch>(ewrite, __float_as_uint(pair_sum(x0, 3)));
-    lds_write_word<4 * 8 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 0)));
-    lds_write_word<4 * 10 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 1)));
-    lds_write_word<4 * 12 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 2)));
-    lds_write_word<4 * 14 * kEPitch>(ewrite, __float_as_uint(pair_sum(x1, 3)));
-    // lane l: its row's threshold and visible blocks, and its 8 sums
+    // the phase's scores into the wave's tile: slot (ms, q4) of lane (r, h)
+    // is tile row 8 (ms - m0) + 2 q4 + h, column r
+    float sc[8];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      sc[q4] = phase_score(x0, q4, exact_c);
+      sc[4 + q4] = phase_score(x1, q4, exact_c);
+    }
+    if constexpr (!decltype(exact_c)::value) note_phase(sc);
+    lds_write_word<4 * 0 * kEPitch>(ewrite, __float_as_uint(sc[0]));
+    lds_write_word<4 * 2 * kEPitch>(ewrite, __float_as_uint(sc[1]));
+    lds_write_word<4 * 4 * kEPitch>(ewrite, __float_as_uint(sc[2]));
+    lds_write_word<4 * 6 * kEPitch>(ewrite, __float_as_uint(sc[3]));
+    lds_write_word<4 * 8 * kEPitch>(ewrite, __float_as_uint(sc[4]));
+    lds_write_word<4 * 10 * kEPitch>(ewrite, __float_as_uint(sc[5]));
+    lds_write_word<4 * 12 * kEPitch>(ewrite, __float_as_uint(sc[6]));
+    lds_write_word<4 * 14 * kEPitch>(ewrite, __float_as_uint(sc[7]));
+    // lane l: its row's threshold and visible blocks, and its 8 scores
     const uint32_t prow = 32 * m + 8 * m0 + er;  // group row
     uint32_t t, nv;
     u32x4_t sums;
@@ -789,13 +780,16 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
     else
       emit8(std::integral_constant<bool, true>{});
   };
-  auto epilogue = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast) {
+  auto epilogue = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast,
+                      auto exact_c) {
     if constexpr (EMIT)
-      pair_emit(x0, x1, m0c, nb0, live, fast);
+      pair_emit(x0, x1, m0c, nb0, live, fast, exact_c);
     else
-      pair_store(x0, x1, decltype(m0c)::value, nb0, live, fast);
+      pair_store(x0, x1, decltype(m0c)::value, nb0, live, fast, exact_c);
   };
 
+#pragma unroll
+  for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t);
   f32x16_t acc[4];
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms)
@@ -826,7 +820,8 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       bf[7] = lds_read16<128>(b3);
     }
     // phase A: the previous step's acc[2..3] (dropped in the first step)
-    epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin);
+    epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, step > 0, step > 0 && prev_nb0 + TILE <= nmin,
+             std::false_type{});
     lds_wait8(bf);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -839,7 +834,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
       acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
     }
-    epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin);
+    epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin, std::false_type{});
     // Tile t + 1 has landed once at most N of this wave's memory operations
     // are outstanding, N = what was issued after its loads: the loads of
     // (D - 2) tiles and the stores of each step since (D - 1 steps in the
@@ -863,9 +858,42 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
     ++step;
     stage = stage + 1 == D ? 0 : stage + 1;
   }
-  epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, true, prev_nb0 + TILE <= nmin);
-  if constexpr (EMIT) store_counts();
+  epilogue(acc[2], acc[3], std::integral_constant<int, 2>{}, prev_nb0, true, prev_nb0 + TILE <= nmin, std::false_type{});
   wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+
+  // score_fast equals score_exact wherever it is finite.  If any lane of the
+  // workgroup produced a non-finite score (rare: NaN or infinite inputs, or
+  // a head dot beyond half the f32 range), the workgroup scores its tiles
+  // again with score_exact, overwriting every score (or re-emitting every
+  // candidate) it wrote.  This pass loads its B fragments straight from
+  // memory, without the ring.
+  if (__syncthreads_or(seen != 0u ? 1 : 0)) {
+    ecnt0 = 0u;
+    ecnt1 = 0u;
+    // lane values recomputed here, so that none of them stays live across
+    // the ring loop above
+    int t2 = threadIdx.x;
+    asm volatile("" : "+v"(t2));
+    const int col2 = 32 * ((t2 >> 6) / WM) + (t2 & 31), h2 = (t2 & 63) >> 5;
+    for (int nb0 = blk_begin; nb0 < nmax; nb0 += stride) {
+      const int c = min(nb0 + col2, nmax - 1);  // columns past nmax are never stored
+      const uint16_t* krow = a.pooled + static_cast<int64_t>(c) * a.bstride * kHeadDim + 8 * h2;
+      bf16x8_t bf[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) bf[ks] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ks);
+      f32x16_t x[4];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        x[ms] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) x[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms][ks], bf[ks], x[ms], 0, 0, 0);
+      }
+      const bool fast = nb0 + TILE <= nmin;
+      epilogue(x[0], x[1], std::integral_constant<int, 0>{}, nb0, true, fast, std::true_type{});
+      epilogue(x[2], x[3], std::integral_constant<int, 2>{}, nb0, true, fast, std::true_type{});
+    }
+  }
+  if constexpr (EMIT) store_counts();
 }
 
 // Workgroups: `target` in all, at least one tile each; a row group's splits

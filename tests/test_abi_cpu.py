@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 7
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 8
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
@@ -377,3 +377,17 @@ def test_score_prepped_refusals(lib):
     assert score_prepped(lib, scores_len=127) == CAP
     assert score_prepped(lib, tokens=262148, score_cols=65537, scores_len=8 * 65537) == CAP
     assert score_prepped(lib, rows=2**40, scores_len=2**62, score_cols=2**20) == CAP
+
+
+def test_fused_fallback_flags_lie_inside_the_workspace(lib):
+    """qsa_score_select_flags_offset: an aligned int32 [rows] array inside the
+    fused call's workspace; the workspace-size refusals apply."""
+    for rows, T, b in ((8192, 65536, 2048), (8, 64, 4), (301, 65543, 2048), (1024, 65536, 64)):
+        n = lib.qsa_score_select_workspace_bytes(rows, T, b)
+        off = lib.qsa_score_select_flags_offset(rows, T, b)
+        assert 0 < off and off % 256 == 0 and off + 4 * rows <= n, (rows, T, b, off, n)
+    assert lib.qsa_score_select_flags_offset(0, 64, 4) == 0
+    assert lib.qsa_score_select_flags_offset(8, 0, 4) == 0
+    assert lib.qsa_score_select_flags_offset(8, 64, 6) == BUDGET
+    assert lib.qsa_score_select_flags_offset(-1, 64, 4) == EXTENT
+    assert lib.qsa_score_select_flags_offset(8, 262148, 4) == CAP

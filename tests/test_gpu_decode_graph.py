@@ -1,15 +1,19 @@
 """A graph-capturable decode step: pool_window -> prep_dev -> score_dev ->
 select_indices_dev -> gather, with the live cache length in a device word.
 
-Checked against the host-count calls (each of which is held to the oracle by
-the other GPU tests): eagerly at several lengths, then as one captured HIP
-graph replayed while the cache grows, with eager work and synchronisation
-between replays and every replay compared."""
+Checked at every cache length, eagerly and as one captured HIP graph
+replayed while the cache grows (eager work and synchronisation between
+replays, every replay compared), against the oracle: pooled keys and
+prepared queries bit-exact, scores within 5e-3, index lists equal to the
+oracle's or differing only at blocks within 5e-3 of a row's cut, and the
+gathered K/V and page table bit-exact against the oracle's gather of the
+lists.  The host-count calls give the same bytes again."""
 
 import numpy as np
 import pytest
 import torch
 
+import oracle as O
 import sparse_attention_token_qsa_amd as qsa
 from tests.gpu_util import DEV, note, workload
 
@@ -28,14 +32,18 @@ class Setup:
         self.w = w
         g = torch.Generator().manual_seed(4321)
         raw = torch.randn((CEIL, 128), generator=g).to(torch.bfloat16)
+        self.raw_np = raw.view(torch.int16).numpy().view(np.uint16).copy()
         self.raw = raw.view(torch.int16).to(DEV)
         self.wk = torch.from_numpy(w["k_norm_w"].view(np.int16)).to(DEV)
         self.wq = torch.from_numpy(w["q_norm_w"].view(np.int16)).to(DEV)
         self.q = torch.from_numpy(w["queries"][:ROWS].reshape(ROWS, 512).view(np.int16)).to(DEV)
         n_pages = CEIL // PAGE
-        self.kc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE, KV_DIM), dtype=torch.int16, generator=g).to(DEV)
-        self.vc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE, KV_DIM), dtype=torch.int16, generator=g).to(DEV)
-        self.table = torch.randperm(n_pages, generator=g).to(torch.int32).to(DEV)
+        kc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE, KV_DIM), dtype=torch.int16, generator=g)
+        vc = torch.randint(-(1 << 15), 1 << 15, (n_pages, PAGE, KV_DIM), dtype=torch.int16, generator=g)
+        table = torch.randperm(n_pages, generator=g).to(torch.int32)
+        self.kc_np, self.vc_np = kc.numpy().view(np.uint16), vc.numpy().view(np.uint16)
+        self.table_np = table.numpy()
+        self.kc, self.vc, self.table = kc.to(DEV), vc.to(DEV), table.to(DEV)
         self.n_pages = n_pages
         self.slots = -(-(BUDGET + 3) // PAGE) * PAGE
 
@@ -88,6 +96,68 @@ class Setup:
                           b["tab"], b["st"])
 
 
+class OracleRef:
+    """The oracle's pooled keys of the whole ceiling (a block depends only
+    on its own four tokens), and per cache length the oracle's prepared
+    queries, scores and index lists of the step's rows at position T - 1."""
+
+    def __init__(self, s):
+        self.s = s
+        w = s.w
+        self.pooled = O.pool_keys(s.raw_np, w["k_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+        self.q = w["queries"][:ROWS]
+
+    def at(self, T):
+        w = self.s.w
+        pos = np.full(ROWS, T - 1, dtype=np.int32)
+        qhat = O.prep_queries(self.q, pos, w["q_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+        sc = O.score_rows(qhat, pos, self.pooled[: T // 4], T)
+        cols = CEIL // 4
+        dense = np.full((ROWS, cols), np.nan, np.float32)
+        for r, v in enumerate(sc):
+            dense[r, : len(v)] = v
+        idx, cnt, st = O.select_indices(dense, cols, pos, T, BUDGET)
+        assert st == 0
+        return qhat, sc, idx, cnt
+
+
+def assert_oracle(got, oref, T, label):
+    """The step's outputs at cache length T against the oracle."""
+    n = T // 4
+    qhat, sc, idx, cnt = oref.at(T)
+    pooled = got["pooled"][:n].cpu().numpy().view(np.uint16)
+    assert np.array_equal(pooled, oref.pooled[:n]), f"{label}: pooled keys differ from the oracle at T={T}"
+    assert np.array_equal(got["qhat"].cpu().numpy().view(np.uint16), qhat), f"{label}: qhat differs at T={T}"
+    gs = got["scores"].view(ROWS, CEIL // 4)[:, :n].cpu().numpy().astype(np.float64)
+    for r in range(ROWS):
+        assert np.max(np.abs(gs[r] - sc[r])) <= 5e-3, f"{label}: scores past the bound at T={T}"
+    gi = got["idx"].cpu().numpy()
+    gc = got["counts"].cpu().numpy()
+    p = T - 1
+    keep = min(BUDGET // 4, n)
+    tail = (p + 1) % 4
+    for r in range(ROWS):
+        assert gc[r] == cnt[r] == 4 * keep + tail, f"{label}: count at T={T}"
+        if np.array_equal(gi[r, : BUDGET + 3], idx[r]):
+            continue
+        lst = gi[r, : gc[r]]
+        assert np.all(gi[r, gc[r]: BUDGET + 3] == -1)
+        assert np.all(np.diff(lst) > 0) and np.array_equal(lst[4 * keep:], np.arange(4 * n, p + 1))
+        gb = lst[: 4 * keep].reshape(keep, 4)
+        assert np.all(gb % 4 == np.arange(4)) and np.all(gb[:, 1:] - gb[:, :1] == np.arange(1, 4))
+        gset, wset = set(gb[:, 0] // 4), set(idx[r, : 4 * keep: 4] // 4)
+        cut = np.sort(sc[r])[::-1][keep - 1]
+        diff = np.array(sorted(gset ^ wset))
+        assert np.all(np.abs(sc[r][diff].astype(np.float64) - cut) <= 5e-3), f"{label}: lists at T={T}"
+    s = oref.s
+    ko, vo, tab, st = O.gather_kv(s.kc_np, s.vc_np, PAGE, s.table_np, 0, s.n_pages, gi, gi.shape[1], gc, ROWS,
+                                  s.slots)
+    assert st == 0
+    assert np.array_equal(got["ko"].cpu().numpy().view(np.uint16), ko), f"{label}: gathered K at T={T}"
+    assert np.array_equal(got["vo"].cpu().numpy().view(np.uint16), vo), f"{label}: gathered V at T={T}"
+    assert np.array_equal(got["tab"].cpu().numpy(), tab), f"{label}: page table at T={T}"
+
+
 def assert_same(got, ref, T, label):
     n = T // 4
     pooled_ok = torch.equal(got["pooled"][:n], ref["pooled"][:n])
@@ -104,6 +174,7 @@ def assert_same(got, ref, T, label):
 
 def test_device_geometry_calls_equal_host_count_calls():
     s = Setup()
+    oref = OracleRef(s)
     b = s.buffers()
     T0 = CEIL - 200
     rd, th, eps = s.rope()
@@ -116,11 +187,13 @@ def test_device_geometry_calls_equal_host_count_calls():
         s.step(b)
         torch.cuda.synchronize()
         assert int(b["st"].item()) == 0
+        assert_oracle(b, oref, T, "eager")
         assert_same(b, s.reference(T), T, "eager")
 
 
 def test_captured_decode_step_replays_as_the_cache_grows():
     s = Setup()
+    oref = OracleRef(s)
     b = s.buffers()
     T0 = CEIL - 120
     rd, th, eps = s.rope()
@@ -151,6 +224,7 @@ def test_captured_decode_step_replays_as_the_cache_grows():
         graph.replay()
         torch.cuda.synchronize()
         assert int(b["st"].item()) == 0
+        assert_oracle(b, oref, T, f"replay {k}")
         assert_same(b, s.reference(T), T, f"replay {k}")
 
 

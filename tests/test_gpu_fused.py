@@ -38,7 +38,10 @@ def separate(qhat, pos, pooled, T, budget):
     return mask, int(st.item())
 
 
-def fused(qhat, pos, pooled, T, budget, ws=None, fill=0x5A):
+def fused(qhat, pos, pooled, T, budget, ws=None, fill=0x5A, flags=False):
+    """Mask (device) and status of qsa_score_select_mask; with flags=True
+    also the per-row fallback flags it leaves in its workspace (1: the row
+    was scored and selected in full)."""
     rows = pos.numel()
     n = qsa.qsa_score_select_workspace_bytes(rows, T, budget)
     if ws is None:
@@ -48,18 +51,23 @@ def fused(qhat, pos, pooled, T, budget, ws=None, fill=0x5A):
     st = status_word()
     qsa.qsa_score_select_mask(qhat, pos, pooled, T, budget, mask, st, ws)
     torch.cuda.synchronize()
-    return mask, int(st.item())
+    if not flags:
+        return mask, int(st.item())
+    off = qsa.qsa_score_select_flags_offset(rows, T, budget)
+    fl = ws[off: off + 4 * rows].view(torch.int32).cpu().numpy()
+    return mask, int(st.item()), fl
 
 
-def assert_same(qhat, pos, pooled, T, budget, label, ws=None):
+def assert_same(qhat, pos, pooled, T, budget, label, ws=None, with_flags=False):
     note(f"fused vs separate: {label}: {pos.numel()} rows, {T} tokens, budget {budget}")
-    mf, sf = fused(qhat, pos, pooled, T, budget, ws=ws)
+    out = fused(qhat, pos, pooled, T, budget, ws=ws, flags=with_flags)
+    mf, sf = out[0], out[1]
     ms, ss = separate(qhat, pos, pooled, T, budget)
     assert sf == ss, (sf, ss)
     if not torch.equal(mf, ms):
         bad = torch.nonzero((mf != ms).any(dim=1)).flatten()[:8].tolist()
         raise AssertionError(f"{label}: masks differ in rows {bad}")
-    return mf, sf
+    return out
 
 
 def prepped(w, pos=None, q=None):
@@ -112,8 +120,11 @@ def test_fused_fallback_when_every_score_ties():
     sel = rng.choice(len(w["pos"]), size=256, replace=False)
     p = w["pos"][sel]
     qhat = prepped(w, pos=p, q=w["queries"][sel])
-    mf, st = assert_same(qhat, i32_dev(p), pooled, T, 2048, "all ties")
+    mf, st, fl = assert_same(qhat, i32_dev(p), pooled, T, 2048, "all ties", with_flags=True)
     assert st == 0
+    # every truncating row fell back to the full path
+    n_all = (p.astype(np.int64) + 1) // 4
+    assert np.array_equal(fl, (n_all > 512).astype(np.int32))
     # lowest indices win ties: blocks 0..511, then the tail
     row = mf[0].cpu().numpy()
     n = (int(p[0]) + 1) // 4
@@ -137,8 +148,9 @@ def test_fused_fallback_when_the_sample_overrates_the_row():
     qh = np.tile(np.concatenate([hi] * 4), (R, 1)).astype(np.float32)
     qh += 0.05 * rng.standard_normal(qh.shape).astype(np.float32)
     qhat = torch.from_numpy(qh).to(DEV).to(torch.bfloat16).view(torch.int16).reshape(R, 4, 128).contiguous()
-    _, st = assert_same(qhat, i32_dev(p), pooled, T, 2048, "overrated sample")
+    _, st, fl = assert_same(qhat, i32_dev(p), pooled, T, 2048, "overrated sample", with_flags=True)
     assert st == 0
+    assert np.all(fl == 1), "every row's sampled threshold admits too few blocks"
 
 
 def test_fused_rows_across_the_budget_and_tiny_caches():
@@ -206,3 +218,40 @@ def test_fused_against_the_oracle():
         wb = want_mask[r][: 4 * n].reshape(n, 4)[:, 0]
         diff = np.nonzero(gb != wb)[0]
         assert np.all(np.abs(s[diff].astype(np.float64) - cut) <= 5e-3), (r, diff[:8])
+
+
+def test_fused_sampled_threshold_against_the_oracle():
+    """1024 consecutive rows of the prefill chunk over 64k (ternary keys and
+    queries: many exact score ties), pooled keys from the oracle.  Every row
+    truncates and has over 900 sampled blocks, so its threshold comes from
+    the samples and the row is selected from its candidates (its fallback
+    flag stays 0).  Masks equal the oracle's, or keep the right number of
+    whole blocks plus the tail and differ from it only at blocks within 5e-3
+    of the row's cut."""
+    from tests import oracle_cache as C
+    w = workload(5)
+    T = w["tokens"]
+    pos, q, want_sc, want_mask, _, _ = C.prefill_slice()
+    qhat, st = gpu_prep(w, pos=pos, q=q)
+    assert st == 0
+    note(f"fused vs oracle: {len(pos)} prefill rows over {T} tokens")
+    mask, st, fl = fused(qhat, i32_dev(pos), u16_dev(C.pooled(5)), T, w["budget"], flags=True)
+    assert st == 0
+    assert np.all(fl == 0), f"{int(fl.sum())} rows fell back"
+    mask = mask.cpu().numpy()
+    loose = 0
+    for r in range(len(pos)):
+        p = int(pos[r])
+        n = (p + 1) // 4
+        if np.array_equal(mask[r], want_mask[r]):
+            continue
+        s = want_sc[r, :n].astype(np.float64)
+        keep = min(w["budget"] // 4, n)
+        cut = np.sort(s)[::-1][keep - 1]
+        gb = mask[r][: 4 * n].reshape(n, 4)[:, 0]
+        wb = want_mask[r][: 4 * n].reshape(n, 4)[:, 0]
+        assert gb.sum() == keep and np.all(mask[r][4 * n: p + 1] == 1) and not mask[r][p + 1:].any()
+        diff = np.nonzero(gb != wb)[0]
+        assert np.all(np.abs(s[diff] - cut) <= 5e-3), (r, diff[:8])
+        loose += 1
+    note(f"  rows differing only at the cut: {loose} of {len(pos)}")

@@ -212,6 +212,75 @@ def test_select_longest_supported_row():
         assert st == 0 and np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("copies", [1, 2])
+def test_select_prefill_batch_on_oracle_scores_bit_exact(copies):
+    """The benchmarked prefill select: 1024 rows of the prefill chunk over 64k
+    (ternary keys and queries, many exact ties), fed the oracle's scores as
+    one batch of 1024 * copies rows (the oracle rows repeated), so the
+    launch is the prefill one: 512 threads per row with the two-per-thread
+    prefilter, 16-byte loads and stores, and rows visited in the 128-row
+    group order of a 1024 k-row batch.  Masks, index lists and counts are
+    bit-exact against the oracle's, and so is the split-capable entry point
+    (which takes the same kernel for this many rows)."""
+    from tests import oracle_cache as C
+    w = workload(5)
+    T = w["tokens"]
+    cols = T // 4
+    pos1, _, sc1, mask1, idx1, cnt1 = C.prefill_slice()
+    pos = np.tile(pos1, copies)
+    sc = np.tile(sc1, (copies, 1))
+    note(f"select, prefill batch on oracle scores: {len(pos)} rows over {T} tokens")
+    got, gst = gpu_select(sc, cols, pos, T, w["budget"])
+    assert gst == 0
+    bad = [r for r in range(len(pos)) if not np.array_equal(got[r], mask1[r % len(pos1)])]
+    assert not bad, (bad[:5], pos[bad[:5]])
+    got_ws, gst, nbytes = gpu_select_ws(sc, cols, pos, T, w["budget"])
+    assert gst == 0 and nbytes == 0 and np.array_equal(got_ws, got)
+    gi, gc, gst = gpu_select_indices(sc, cols, pos, T, w["budget"])
+    assert gst == 0
+    assert np.array_equal(gc, np.tile(cnt1, copies))
+    assert np.array_equal(gi, np.tile(idx1, (copies, 1)))
+
+
+def _template_positions(T):
+    """Sixteen row positions over a T-token cache: the last tokens (every
+    tail length), around the budget boundary, the middle, tiny rows."""
+    p = [T - 1, T - 2, T - 3, T - 4, T - 5, T // 2 + 1, T // 2 - 1, 3 * T // 4, T // 4,
+         2047, 2050, 2051, 2055, 67, 4, 0]
+    return np.array([min(x, T - 1) for x in p], dtype=np.int32)
+
+
+@pytest.mark.parametrize("rows", [16, 1024])
+@pytest.mark.parametrize("T", [4096, 8192, 16384, 32768, 65536, 131072, 262144])
+def test_select_fixture_batches_reach_every_template_bit_exact(T, rows):
+    """The selector fixtures (signed zeros, ties, low-byte keys, wild
+    magnitudes, all equal, random, non-finite) over caches of 4k to 256k
+    tokens (multiples of 16: the vectorised load and store forms), as
+    batches of 16 and 1024 rows (the 16 fixture rows repeated): every
+    one-workgroup-per-row select template, with and without the prefilter,
+    in index order and in the group order of 1024-row batches.  Masks,
+    index lists and counts bit-exact against the oracle's on every row."""
+    pos16 = _template_positions(T)
+    reps = rows // len(pos16)
+    for kind in ("zeros", "ties", "lowbyte", "wild", "equal", "random", "poison"):
+        sc16, cols, p16, T2 = synth.selector_fixture(kind, positions=pos16)
+        assert T2 == T and cols == T // 4
+        sc = np.tile(sc16, (reps, 1))
+        pos = np.tile(p16, reps)
+        for budget in (2048, 64, 4):
+            want, wst = O.select_mask(sc16, cols, p16, T, budget)
+            wi, wc, wst2 = O.select_indices(sc16, cols, p16, T, budget)
+            note(f"select fixture batch: {kind}, {rows} rows over {T} tokens, budget {budget}")
+            got, gst = gpu_select(sc, cols, pos, T, budget)
+            assert gst == wst
+            bad = [r for r in range(len(pos)) if not np.array_equal(got[r], want[r % 16])]
+            assert not bad, (kind, budget, bad[:5], pos[bad[:5]])
+            gi, gc, gst = gpu_select_indices(sc, cols, pos, T, budget)
+            assert gst == wst2
+            assert np.array_equal(gc, np.tile(wc, reps)), (kind, budget)
+            assert np.array_equal(gi, np.tile(wi, (reps, 1))), (kind, budget)
+
+
 # ------------------------------------------------- select, index lists ----
 
 def _check_indices(got, gcnt, want, wcnt, budget, stride):
@@ -589,11 +658,13 @@ def test_score_long_batches_ragged_rows_bad_positions_nan_key():
 
 def test_score_full_prefill_chunk_ring_equals_one_call_scorer():
     """Every score of the 8192-row prefill chunk over 64k (125.8 M pairs, the
-    benchmarked launch: 128-row ring scorer, steady-state steps on interior
-    tiles) equals the one-call scorer's bit for bit (a different kernel: 32
-    rows per workgroup, queries normed and roped in its prologue), and the
-    columns past each row's prefix keep their sentinel.  Compared on the
-    device."""
+    benchmarked launch: the 128-row ring scorer, one step loop over 32-block
+    tiles streamed through a four-stage LDS ring) equals the one-call
+    scorer's bit for bit (a different kernel: 32 rows per workgroup, queries
+    normed and roped in its prologue), and the columns past each row's
+    prefix keep their sentinel.  Compared on the device; the oracle checks
+    of the same launch are in test_end_to_end_masks and
+    test_ring_scorer_prefill_rows_within_bound."""
     w = workload(5)
     T = w["tokens"]
     rows = len(w["pos"])
@@ -620,6 +691,159 @@ def test_score_full_prefill_chunk_ring_equals_one_call_scorer():
     assert bool((a.view(rows, cols)[outside] == -7.25).all())
 
 
+def test_ring_scorer_prefill_rows_within_bound():
+    """The ring scorer (128 rows per workgroup, the prefill launch) on 1024
+    consecutive rows of the prefill chunk over 64k, against the oracle:
+    15.8 M scores within 5e-3, nothing written past any row's prefix."""
+    from tests import oracle_cache as C
+    w = workload(5)
+    T = w["tokens"]
+    cols = T // 4
+    pos, q, want, _, _, _ = C.prefill_slice()
+    note(f"ring scorer vs oracle: {len(pos)} rows over {T} tokens")
+    got, st = gpu_scores_prepped(w, u16_dev(C.pooled(5)), pos=pos, q=q, score_cols=cols)
+    assert st == 0
+    n = (pos.astype(np.int64) + 1) // 4
+    inside = np.arange(cols)[None, :] < n[:, None]
+    assert np.all(got[~inside] == np.float32(-7.25)), "wrote past the visible prefix"
+    worst = float(np.max(np.abs(got[inside].astype(np.float64) - want[inside])))
+    note(f"  max |gpu - oracle| = {worst:.3e}")
+    assert worst <= SCORE_ATOL
+
+
+def _huge_dot_inputs(R, seed=31):
+    """Prepared queries and pooled keys whose head dots reach past half the
+    f32 range (one head: 128 * (1.5e18)^2 ~ 2.9e38 < FLT_MAX) or overflow
+    to -Inf (a key of -1.5e19 against a query of 1.5e18), beside ordinary
+    N(0, 1) values.  T = 256 tokens, rows at the last position."""
+    rng = np.random.default_rng(seed)
+    T = 256
+    nb = T // 4
+    keys = rng.standard_normal((nb, 128)).astype(np.float32)
+    keys[5] = 1.5e18
+    keys[9] = -1.5e19
+    keys[20] = 1.5e18
+    keys[20, :64] = -1.5e18          # a zero-sum huge key: the dot cancels exactly
+    qs = rng.standard_normal((R, 4, 128)).astype(np.float32)
+    qs[:, 0] = 1.5e18                 # head 0: 2.9e38 on block 5, -Inf on block 9
+    qs[::3, 1] = 1.5e18               # every third row: two such heads, the sum overflows
+    qs[1::3, 2] = -1.5e18             # others: a huge negative head (relu 0)
+    pos = np.full(R, T - 1, dtype=np.int32)
+    return T, synth.bf16_bits(keys), synth.bf16_bits(qs), pos
+
+
+def _compare_huge(got, want, pos):
+    """Finite oracle scores: within 5e-3 + 2^-16 relative (f32 accumulation
+    of 128 products near 1e36); non-finite ones: the same class."""
+    for r, s in enumerate(want):
+        n = len(s)
+        g = got[r, :n].astype(np.float64)
+        fin = np.isfinite(s)
+        assert np.array_equal(np.isnan(g[~fin]), np.isnan(s[~fin])), r
+        assert np.array_equal(g[~fin & ~np.isnan(s)], s[~fin & ~np.isnan(s)].astype(np.float64)), r
+        assert np.all(np.isfinite(g[fin])), (r, np.nonzero(~np.isfinite(g) & fin)[0][:5])
+        err = np.abs(g[fin] - s[fin])
+        assert np.all(err <= 5e-3 + 2.0 ** -16 * np.abs(s[fin])), (r, float(err.max()))
+
+
+@pytest.mark.parametrize("R", [8, 70, 130])
+def test_score_head_dots_past_half_range_and_minus_inf(R):
+    """relu is a comparison: a head dot of -Inf contributes 0, and head dots
+    above 2^127 (whose doubled relu terms would overflow) keep their finite
+    score, as in the oracle; two such heads overflow the f32 head sum to
+    +Inf there too.  Prepared queries through the decode kernels (8 and 70
+    rows) and the ring scorer (130 rows)."""
+    T, keys, qs, pos = _huge_dot_inputs(R)
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)
+        want = O.score_rows(qs, pos, keys, T)
+    assert any(np.isinf(s).any() for s in want) and all(np.isfinite(s[5]) for s in want[1::3])
+    cols = T // 4
+    scores = torch.full((R * cols,), -7.25, dtype=torch.float32, device=DEV)
+    st = status_word()
+    note(f"score: huge head dots, {R} prepared rows")
+    qsa.qsa_score_prepped(u16_dev(qs.reshape(R, 4, 128)), i32_dev(pos), u16_dev(keys), T, scores, cols, st)
+    assert qsa.check_status(st) == 0
+    _compare_huge(scores.cpu().numpy().reshape(R, cols), want, pos)
+
+
+def test_score_rows_huge_norm_weights():
+    """The one-call scorer with a (1 + w) query weight of 1.5e18 on every
+    channel and no rotary channels.  Head 0 is constant (normed to 1.5e18 on
+    every channel), heads 1 and 2 one-hot with opposite signs (1.7e19 on one
+    channel), head 3 zero: against the constant keys head 0 reaches 2.9e38
+    (and the relu sum 3.1e38, whose doubled form overflows) or -Inf, whose
+    doubled form is NaN; the oracle's finite scores stay finite and within
+    bound.  Every dot is deterministic: no partial sum of any accumulation
+    order overflows unless the exact one does."""
+    R = 40
+    T, keys, _, pos = _huge_dot_inputs(R)
+    q = np.zeros((R, 4, 128), np.float32)
+    q[:, 0] = 1.0
+    q[:, 1, 7] = 1.0
+    q[:, 2, 9] = -1.0
+    qb = synth.bf16_bits(q)
+    wq = synth.bf16_bits(np.full(128, 1.5e18, np.float32))
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)
+        qhat = O.prep_queries(qb, pos, wq, 0, 1e4, 1e-6)
+        want = O.score_rows(qhat, pos, keys, T)
+    cols = T // 4
+    scores = torch.full((R * cols,), -7.25, dtype=torch.float32, device=DEV)
+    st = status_word()
+    note("score: one-call scorer, huge query norm weight")
+    qsa.qsa_score_rows(u16_dev(qb.reshape(R, 512)), i32_dev(pos), u16_dev(wq), 0, 1e4, 1e-6, u16_dev(keys), T,
+                       scores, cols, st)
+    assert qsa.check_status(st) == 0
+    _compare_huge(scores.cpu().numpy().reshape(R, cols), want, pos)
+
+
+def _wide_range(shape, rng):
+    """bf16 values with magnitudes spread over 2^-60 .. 2^60 (the double sum
+    of their squares is no longer exact), random signs, some zeros."""
+    mag = np.exp2(rng.uniform(-60, 60, size=shape)).astype(np.float32)
+    v = mag * np.where(rng.random(shape) < 0.5, -1.0, 1.0).astype(np.float32)
+    v[rng.random(shape) < 0.02] = 0.0
+    return v.astype(np.float32)
+
+
+def test_pool_and_prep_wide_dynamic_range_bit_exact():
+    """Keys whose channels span 2^120 in magnitude within a block, keys with
+    one outlier channel (1e3 against 1e-4: a span past 2^18), and queries of
+    the same kinds: pooled keys and prepared queries bit-exact against the
+    oracle (both sum the squares in double; past a 2^18 span the sum is
+    rounded, in different orders, and these seeded inputs are checked to
+    give identical bf16 outputs)."""
+    rng = np.random.default_rng(41)
+    T = 4096
+    raw = _wide_range((T, 128), rng)
+    out = rng.standard_normal((T // 2, 128)).astype(np.float32) * np.float32(1e-4)
+    out[:, 17] = 1e3
+    raw[: T // 2] = out
+    rawb = synth.bf16_bits(raw)
+    wk = synth.bf16_bits((rng.standard_normal(128) * 0.05).astype(np.float32))
+    w = dict(workload(2), raw_keys=rawb, k_norm_w=wk)
+    note("pool: wide dynamic range")
+    got = u16_host(gpu_pool(w))
+    want = O.pool_keys(rawb, wk, 64, 1e4, 1e-6)
+    diff = np.nonzero(got != want)
+    assert len(diff[0]) == 0, (len(diff[0]), diff[0][:8], diff[1][:8])
+    R = 256
+    q = _wide_range((R, 4, 128), rng)
+    q[: R // 2, :, :] = rng.standard_normal((R // 2, 4, 128)).astype(np.float32) * np.float32(1e-4)
+    q[: R // 2, :, 3] = 1e3
+    qb = synth.bf16_bits(q)
+    pos = rng.integers(0, T, size=R).astype(np.int32)
+    note("prep: wide dynamic range")
+    qhat, st = gpu_prep(dict(w, queries=qb), pos=pos, q=qb)
+    assert st == 0
+    wantq = O.prep_queries(qb, pos, w["q_norm_w"], 64, 1e4, 1e-6)
+    diff = np.nonzero(u16_host(qhat) != wantq)
+    assert len(diff[0]) == 0, (len(diff[0]), diff[0][:8])
+
+
 # ------------------------------------------------------------ end to end ----
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
@@ -638,6 +862,15 @@ def test_end_to_end_masks(wid):
     assert st == 0
     rows = sample_rows(wid)
     want_scores = oracle_sample_scores(wid)
+    # the scores of this launch (for the 8192-row chunk: the benchmarked ring
+    # scorer over the whole batch) on the sampled rows, against the oracle
+    worst = 0.0
+    for i, r in enumerate(rows):
+        n = len(want_scores[i])
+        if n:
+            worst = max(worst, float(np.max(np.abs(scores[r, :n].astype(np.float64) - want_scores[i]))))
+    note(f"  max |gpu - oracle| over the sampled rows = {worst:.3e}")
+    assert worst <= SCORE_ATOL
     want_dense = dense(want_scores, cols)
     want_mask, _ = O.select_mask(want_dense, cols, w["pos"][rows], T, w["budget"])
     loose = 0
