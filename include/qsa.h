@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 8
+#define QSA_ABI_VERSION 9
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -242,6 +242,29 @@ int qsa_select_mask_ws(const float* scores, int64_t score_cols, int64_t scores_l
                        const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
                        uint8_t* mask, int32_t* dev_status, void* workspace,
                        int64_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch array qsa_select_mask_noalloc uses (per GPU). */
+#define QSA_NOALLOC_SCRATCH_BYTES (8 << 20)
+
+/*
+ * qsa_select_mask_noalloc -- qsa_select_mask_ws without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid allocation): same kept sets, mask
+ * bytes and status bits.  When the split select runs (the rows and tokens
+ * for which qsa_select_workspace_bytes(rows, tokens) > 0) its workspace is a
+ * library-owned device array of QSA_NOALLOC_SCRATCH_BYTES, one per GPU, held
+ * until the process ends; otherwise the call is qsa_select_mask.  The call
+ * allocates and frees nothing; its first call on a device looks up that
+ * device's array (with that device current).  Calls that overlap on one
+ * GPU share the array and race: serialise them (one stream, or events).
+ * Refusals: those of qsa_select_mask, and QSA_ERR_CAPACITY when the split
+ * select would need more than QSA_NOALLOC_SCRATCH_BYTES (about 113 rows at
+ * QSA_MAX_TOKENS tokens, 120 rows at 262144); QSA_ERR_LAUNCH if the array's
+ * address cannot be obtained.
+ */
+int qsa_select_mask_noalloc(const float* scores, int64_t score_cols, int64_t scores_len,
+                            const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                            uint8_t* mask, int32_t* dev_status, void* stream);
 
 /*
  * qsa_score_select_workspace_bytes -- device workspace qsa_score_select_mask

@@ -21,7 +21,8 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
 
 __all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
-           "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_flags_offset",
+           "qsa_select_mask_ws", "qsa_select_mask_noalloc", "qsa_score_select_workspace_bytes",
+           "qsa_score_select_flags_offset",
            "qsa_score_select_mask",
            "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
            "qsa_select_indices_dev", "qsa_select_indices_ws",
@@ -233,6 +234,25 @@ def qsa_select_mask_ws(scores: torch.Tensor, score_cols: int, pos: torch.Tensor,
     _check(lib.qsa_select_mask_ws(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
                                   budget, _ptr(mask), _ptr(dev_status), _ptr(workspace), ws_bytes,
                                   _stream_ptr(stream)), "qsa_select_mask_ws")
+
+
+def qsa_select_mask_noalloc(scores: torch.Tensor, score_cols: int, pos: torch.Tensor, tokens: int,
+                            budget: int, mask: torch.Tensor, dev_status: torch.Tensor, stream=None) -> None:
+    """qsa_select_mask_ws with the library's own device scratch in place of a
+    workspace: allocates nothing (for graph capture and allocation-free
+    loops).  Calls overlapping on one GPU share the scratch and race."""
+    _dev(scores, "scores", (torch.float32,))
+    _dev(pos, "pos", (torch.int32,))
+    _dev(mask, "mask", (torch.uint8,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    rows = pos.numel()
+    _need(pos.is_contiguous(), "pos must be contiguous")
+    _need(scores.is_contiguous(), "scores must be contiguous")
+    _need(mask.is_contiguous() and mask.numel() >= rows * tokens, "mask must be contiguous [rows, tokens]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    _check(load().qsa_select_mask_noalloc(_ptr(scores), score_cols, scores.numel(), _ptr(pos), rows, tokens,
+                                          budget, _ptr(mask), _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_select_mask_noalloc")
 
 
 def qsa_score_select_workspace_bytes(rows: int, tokens: int, budget: int) -> int:

@@ -30,16 +30,18 @@ HEAD_DIM = 128
 RATIO = 4
 MAX_KEEP_BLOCKS = 512
 MAX_TOKENS = 262147
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Every symbol the header declares.
 EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
-           "qsa_select_mask_ws", "qsa_score_select_workspace_bytes", "qsa_score_select_flags_offset",
+           "qsa_select_mask_ws", "qsa_select_mask_noalloc", "qsa_score_select_workspace_bytes",
+           "qsa_score_select_flags_offset",
            "qsa_score_select_mask",
            "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
            "qsa_select_indices_dev", "qsa_select_indices_ws", "qsa_rope_inv_freq", "qsa_strerror",
            "qsa_abi_version")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _lib = None
 
@@ -76,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_select_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_select_mask_ws.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P, I64, P]
     lib.qsa_select_mask_ws.restype = ctypes.c_int
+    lib.qsa_select_mask_noalloc.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P]
+    lib.qsa_select_mask_noalloc.restype = ctypes.c_int
     lib.qsa_score_select_workspace_bytes.argtypes = [I64, I64, I64]
     lib.qsa_score_select_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_score_select_flags_offset.argtypes = [I64, I64, I64]

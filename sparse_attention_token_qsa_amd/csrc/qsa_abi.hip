@@ -223,6 +223,22 @@ int qsa_select_mask_ws(const float* scores, int64_t score_cols, int64_t scores_l
                                                 dev_status, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_select_mask_noalloc(const float* scores, int64_t score_cols, int64_t scores_len,
+                            const int32_t* pos, int64_t rows, int64_t tokens, int64_t budget,
+                            uint8_t* mask, int32_t* dev_status, void* stream) {
+  const int rc = check_select(scores, score_cols, scores_len, pos, rows, tokens, budget, mask, dev_status);
+  if (rc <= 0) return rc;
+  const int keep_max = static_cast<int>(budget / QSA_RATIO);
+  if (!qsa::select_split_pays(rows, tokens))
+    return launch_status(qsa::launch_select(scores, score_cols, pos, rows, tokens, keep_max, mask,
+                                            dev_status, static_cast<hipStream_t>(stream)));
+  if (qsa::select_split_workspace_bytes(rows, tokens) > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_CAPACITY;
+  void* ws = nullptr;
+  if (qsa::noalloc_scratch(&ws) != hipSuccess) return QSA_ERR_LAUNCH;
+  return launch_status(qsa::launch_select_split(scores, score_cols, pos, rows, tokens, keep_max, mask,
+                                                dev_status, ws, static_cast<hipStream_t>(stream)));
+}
+
 int64_t qsa_score_select_workspace_bytes(int64_t rows, int64_t tokens, int64_t budget) {
   if (rows < 0 || tokens < 0) return QSA_ERR_EXTENT;
   if (budget <= 0 || budget % QSA_RATIO != 0 || budget / QSA_RATIO > QSA_MAX_KEEP_BLOCKS)

@@ -53,6 +53,10 @@ int64_t select_split_workspace_bytes(int64_t rows, int64_t tokens);
 hipError_t launch_select_split(const float* scores, int64_t score_cols, const int32_t* pos,
                                int64_t rows, int64_t tokens, int keep_max, uint8_t* mask,
                                int32_t* status, void* workspace, hipStream_t stream);
+// The device address, on the current device, of the library's scratch array
+// for qsa_select_mask_noalloc (QSA_NOALLOC_SCRATCH_BYTES); looked up once per
+// device, no allocation.
+hipError_t noalloc_scratch(void** out);
 // The same split, writing index lists (qsa_select_indices' format).
 hipError_t launch_select_split_indices(const float* scores, int64_t score_cols, const int32_t* pos,
                                        int64_t rows, int64_t tokens, int keep_max, int32_t* idx,

@@ -21,6 +21,8 @@
 //     select_common.h), and the slice's mask bytes: kept blocks, the tail
 //     and the zeros past the row's position.  Every workgroup of a row finds
 //     the same C*, so the slices need no exchange.
+#include <mutex>
+
 #include "../../include/qsa.h"
 #include "qsa_device.h"
 #include "qsa_launch.h"
@@ -588,6 +590,42 @@ hipError_t launch_select_split_indices(const float* scores, int64_t score_cols, 
   a.counts = counts;
   a.status = status;
   return launch_split(a, rows, true, workspace, stream);
+}
+
+// ---- scratch for callers that cannot allocate ---------------------------
+//
+// qsa_select_mask_noalloc runs the split select on this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds
+// its own copy (QSA_NOALLOC_SCRATCH_BYTES) until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress, once per device, on the first call
+// made with that device current, and only that address reaches the kernels.
+// The split kernels write every workspace word they read, so nothing is
+// cleared between calls; calls that overlap on one GPU share the array and
+// race.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace qsa

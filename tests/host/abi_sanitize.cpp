@@ -110,6 +110,12 @@ hipError_t launch_select_split(const float*, int64_t score_cols, const int32_t* 
   return hipSuccess;
 }
 
+hipError_t noalloc_scratch(void** out) {
+  static unsigned char fake_scratch[256] __attribute__((aligned(256)));
+  *out = fake_scratch;  // the stubs never touch it
+  return hipSuccess;
+}
+
 hipError_t launch_select_split_indices(const float*, int64_t score_cols, const int32_t* pos, int64_t rows,
                                        int64_t tokens, int keep_max, int32_t* idx, int64_t idx_stride,
                                        int32_t* counts, int32_t* status, void* workspace, hipStream_t,
@@ -231,6 +237,12 @@ int main() {
   const long l0 = g_launches;
   REQUIRE(qsa_pool_keys(u, 128, 64, u, 64, 1e4f, 1e-6f, 0, 16, (uint16_t*)F, nullptr) == QSA_OK);
   REQUIRE(g_launches == l0 + 1);
+  // the no-allocation select: its scratch limit, then an accepted split call
+  REQUIRE(qsa_select_mask_noalloc((float*)F, 65536, 128 * 65536, (int32_t*)F, 128, 262144, 2048, (uint8_t*)F,
+                                  (int32_t*)F, nullptr) == QSA_ERR_CAPACITY);
+  REQUIRE(qsa_select_mask_noalloc((float*)F, 65536, 16 * 65536, (int32_t*)F, 16, 262144, 2048, (uint8_t*)F,
+                                  (int32_t*)F, nullptr) == QSA_OK);
+  REQUIRE(g_launches == l0 + 2);
   REQUIRE(qsa_pool_keys(u, 128, INT64_MAX, u, 64, 1e4f, 1e-6f, 0, 16, (uint16_t*)F, nullptr) == QSA_ERR_CAPACITY);
   REQUIRE(qsa_select_mask((float*)F, INT64_MAX, INT64_MAX, (int32_t*)F, INT64_MAX, 64, 64, (uint8_t*)F,
                           (int32_t*)F, nullptr) == QSA_ERR_CAPACITY);
@@ -238,7 +250,7 @@ int main() {
                              (int32_t*)F, (int32_t*)F, nullptr) == QSA_ERR_BUDGET);
   REQUIRE(qsa_select_workspace_bytes(INT64_MAX, 262144) == 0);
   REQUIRE(qsa_score_select_workspace_bytes(INT64_MAX, 64, 4) == QSA_ERR_CAPACITY);
-  REQUIRE(g_launches == l0 + 1);
+  REQUIRE(g_launches == l0 + 2);
 
   // the sweep: every entry point, random combinations of extreme extents,
   // bad and good parameters and NULL / fake pointers
@@ -246,7 +258,7 @@ int main() {
   long counted = 0;
   for (int it = 0; it < kIters; ++it) {
     int64_t rc = 0;
-    switch (it % 17) {
+    switch (it % 18) {
       case 0:
         rc = qsa_pool_keys(P<uint16_t>(), any_int(128), any_int(4096), P<uint16_t>(), any_i32(64), any_float(1e4f),
                            any_float(1e-6f), any_int(0), any_int(1024), P<uint16_t>(), nullptr);
@@ -323,8 +335,12 @@ int main() {
       case 16:
         rc = qsa_score_select_flags_offset(any_int(8192), any_int(65536), any_int(2048));
         break;
+      case 17:
+        rc = qsa_select_mask_noalloc(P<float>(), any_int(65536), any_int(16 * 65536), P<int32_t>(), any_int(16),
+                                     any_int(262144), any_int(2048), P<uint8_t>(), P<int32_t>(), nullptr);
+        break;
     }
-    const int k = it % 17;
+    const int k = it % 18;
     const bool size_query = k == 6 || k == 8 || k == 16;
     REQUIRE(size_query ? rc >= -7 : documented(rc));
     ++counted;
