@@ -5,13 +5,15 @@
 // to bf16, then (1 + w) RMSNorm and partial RoPE at the block's first token.
 //
 // Layout: a workgroup of 256 threads pools 16 consecutive blocks; each block
-// is owned by 16 lanes holding 8 channels each, so one block's four 256-byte
-// token rows are read as four 16-byte loads per lane and the pooled 256-byte
-// row leaves as one 16-byte store per lane.  The loads are issued first; the
-// cos/sin of the 16 anchors (one (block, frequency) pair per thread and
-// pass) overlap them.  The RMSNorm statistic is a 16-lane DPP reduction in
-// double; the RoPE partner is read back from the normed row in LDS, so any
-// even rotary_dim works.  Roundings to bf16 use the hardware's
+// is owned by 16 lanes (of one wave) holding 8 channels each, so one block's
+// four 256-byte token rows are read as four 16-byte loads per lane and the
+// pooled 256-byte row leaves as one 16-byte store per lane.  The loads are
+// issued first; each lane's cos/sin (for the rotary pairs g, g + 16, ... it
+// rotates) overlap them.  The RMSNorm statistic is a 16-lane DPP reduction
+// in double.  The RoPE goes pair by pair through the block's row in LDS, so
+// every lane rotates (two pairs each at rotary_dim 64) and any even
+// rotary_dim works; a block's lanes share a wave, so wave-level ordering of
+// the LDS traffic suffices.  Roundings to bf16 use the hardware's
 // round-to-nearest-even conversion; a NaN result is written as 0x7FC0.  The
 // stage is HBM-bound: 1 KiB read and 256 B written per block.
 #include "qsa_device.h"
@@ -55,13 +57,21 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// bf16 NaN test of both halves of a packed word: a half is NaN exactly when
+// its magnitude bits exceed 0x7F80, i.e. reach 0x8000 after adding 0x7F
+// (no carry crosses into the other half).
+__device__ __forceinline__ uint32_t nan_halves(uint32_t d) {
+  return ((d & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u;
+}
+
 template <bool kVec>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t csq[kPoolBlocksPerGroup][kMaxHalfRotary];
-  __shared__ __attribute__((aligned(16))) uint4 ys[kPoolBlocksPerGroup][16];
+  // one 128-channel bf16 row per block slot: the normed key, then (in place)
+  // the rotated channels
+  __shared__ __attribute__((aligned(16))) uint16_t ys[kPoolBlocksPerGroup][kHeadDim];
 
   const int tid = threadIdx.x;
-  const int slot = tid >> 4;  // block slot within the group
+  const int slot = tid >> 4;  // block slot within the group (16 lanes of one wave)
   const int g = tid & 15;     // channel group: channels 8g .. 8g+7
   const int64_t group_first = static_cast<int64_t>(blockIdx.x) * kPoolBlocksPerGroup;
   const int64_t blk = group_first + slot;
@@ -98,13 +108,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) wp[e] = 1.0 + static_cast<double>(bf16_to_f32(a.w[8 * g + e]));
 
-  // cos/sin at every slot's anchor 4b: thread (slot, j) takes frequencies
-  // j, j + 16, ... below rotary_dim / 2.
+  // cos/sin at the anchor 4b for the rotary pairs this lane rotates: pairs
+  // i = g, g + 16, g + 32, g + 48 below rotary_dim / 2 (computed while the
+  // loads are in flight)
   const int rd = a.rp.rotary_dim;
   const int half = rd >> 1;
   const int64_t anchor = kRatio * b;
-  for (int i = g; i < half; i += 16) {
-    csq[slot][i] = rope_cos_sin_bf16x2(anchor, a.rp.inv_freq[i]);
+  uint32_t cs[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = g + 16 * k;
+    cs[k] = i < half ? rope_cos_sin_bf16x2(anchor, a.rp.inv_freq[i]) : 0u;
   }
 
   // f32 mean of the 4 tokens in token order, cast to bf16.
@@ -133,59 +147,50 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
 #pragma clang fp contract(off)
     y[e] = rb_hw(static_cast<float>((static_cast<double>(m[e]) * r) * wp[e]));
   }
-  ys[slot][g] = make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]),
-                           pack2(y[6], y[7]));
-  __syncthreads();
+  uint16_t* row = &ys[slot][0];
+  *reinterpret_cast<uint4*>(row + 8 * g) =
+      make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
+  wave_lds_sync();  // a block's 16 lanes live in one wave
 
-  // Partial RoPE at the block's first token.
-  float o[8];
+  // Partial RoPE at the block's first token, pair by pair: every product and
+  // sum rounds to bf16, o_i = rb(rb(y_i c) - rb(y_{i+h} s)),
+  // o_{i+h} = rb(rb(y_{i+h} c) + rb(y_i s)).  All of the row is read before
+  // any rotated channel is written back in its place.
+  float x0[4], x1[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = y[e];
-  const int c0 = 8 * g;
-  if ((half & 7) == 0) {  // chunks of 8 channels never straddle the halves
-    if (c0 < rd) {
-      const bool first = c0 < half;
-      float yp[8];
-      unpack8(ys[slot][first ? g + (half >> 3) : g - (half >> 3)], yp);
-      const int f0 = first ? c0 : c0 - half;
-      const uint4 cs0 = *reinterpret_cast<const uint4*>(&csq[slot][f0]);
-      const uint4 cs1 = *reinterpret_cast<const uint4*>(&csq[slot][f0 + 4]);
-      const uint32_t cs[8] = {cs0.x, cs0.y, cs0.z, cs0.w, cs1.x, cs1.y, cs1.z, cs1.w};
+  for (int k = 0; k < 4; ++k) {
+    const int i = g + 16 * k;
+    x0[k] = i < half ? bf16_to_f32(row[i]) : 0.0f;
+    x1[k] = i < half ? bf16_to_f32(row[i + half]) : 0.0f;
+  }
+  wave_lds_sync();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+  for (int k = 0; k < 4; ++k) {
 #pragma clang fp contract(off)
-        const float p0 = rb_hw(y[e] * __uint_as_float(cs[e] << 16));
-        const float p1 = rb_hw(yp[e] * __uint_as_float(cs[e] & 0xFFFF0000u));
-        o[e] = first ? p0 - p1 : p0 + p1;
-      }
-    }
-  } else {
-    const uint16_t* yrow = reinterpret_cast<const uint16_t*>(&ys[slot][0]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-#pragma clang fp contract(off)
-      const int c = c0 + e;
-      if (c < rd) {
-        const bool first = c < half;
-        const float yp = bf16_to_f32(yrow[first ? c + half : c - half]);
-        const uint32_t cs = csq[slot][first ? c : c - half];
-        const float p0 = rb_hw(y[e] * __uint_as_float(cs << 16));
-        const float p1 = rb_hw(yp * __uint_as_float(cs & 0xFFFF0000u));
-        o[e] = first ? p0 - p1 : p0 + p1;
-      }
+    const int i = g + 16 * k;
+    if (i < half) {
+      const float c = __uint_as_float(cs[k] << 16);
+      const float sn = __uint_as_float(cs[k] & 0xFFFF0000u);
+      const float o0 = rb_hw(x0[k] * c) - rb_hw(x1[k] * sn);
+      const float o1 = rb_hw(x1[k] * c) + rb_hw(x0[k] * sn);
+      row[i] = static_cast<uint16_t>(pack2(o0, 0.0f) & 0xFFFFu);
+      row[i + half] = static_cast<uint16_t>(pack2(o1, 0.0f) & 0xFFFFu);
     }
   }
+  wave_lds_sync();
   if (live) {
-    uint4 out = make_uint4(pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]),
-                           pack2(o[6], o[7]));
-    bool nan = false;
+    uint4 out = *reinterpret_cast<const uint4*>(row + 8 * g);
+    if (nan_halves(out.x) | nan_halves(out.y) | nan_halves(out.z) | nan_halves(out.w)) {
+      // rare: a non-finite key, weight or norm; NaN is written as 0x7FC0
+      uint32_t wd[4] = {out.x, out.y, out.z, out.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) nan |= o[e] != o[e];
-    if (nan) {  // rare: only a non-finite key, weight or norm gets here
-      out = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                       pack_bf16x2(o[6], o[7]));
+      for (int i = 0; i < 4; ++i) {
+        if (nan_halves(wd[i]) & 0x8000u) wd[i] = (wd[i] & 0xFFFF0000u) | 0x7FC0u;
+        if (nan_halves(wd[i]) & 0x80000000u) wd[i] = (wd[i] & 0x0000FFFFu) | 0x7FC00000u;
+      }
+      out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
-    uint16_t* dst = a.pooled + b * kHeadDim + c0;
+    uint16_t* dst = a.pooled + b * kHeadDim + 8 * g;
     if constexpr (kVec) {
       *reinterpret_cast<uint4*>(dst) = out;
     } else {

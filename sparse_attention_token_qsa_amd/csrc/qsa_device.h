@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qsa_rope_math.h"
+
 namespace qsa {
 
 constexpr int kHeads = 4;
@@ -149,20 +151,32 @@ __device__ __forceinline__ void cos_sin_small_angle(float angle, double& c, doub
 }
 
 // Rotary angle of position `p` at frequency `f`: one f32 product, then cos
-// and sin evaluated in double on that f32 angle, rounded to f32 and then to
-// bf16.  Returned packed: cos in bits 0..15, sin in bits 16..31.  Positions
-// below 2^18 with frequencies at most 1 keep |angle| < 2^18; any other angle
-// goes through the library cos/sin.  Both values are finite (|.| <= 1), so the
+// and sin of that f32 angle rounded to f32 and then to bf16, as if evaluated
+// exactly.  Returned packed: cos in bits 0..15, sin in bits 16..31.  The f32
+// evaluation (cos_sin_f32) decides the bf16 values whenever both lie
+// farther from a bf16 rounding midpoint than its error allowance (about 99.8%
+// of the pairs); the rest are evaluated in double (Cody-Waite below 2^18,
+// the library cos/sin beyond: positions below 2^18 with frequencies at most
+// 1 keep |angle| < 2^18).  Both values are finite (|.| <= 1), so the
 // hardware round-to-nearest-even conversion is the bf16 rounding.
 __device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int64_t p, float f) {
 #pragma clang fp contract(off)
   const float angle = static_cast<float>(p) * f;
-  double sd, cd;
-  if (fabsf(angle) < 262144.0f)
-    cos_sin_small_angle(angle, cd, sd);
-  else
-    sincos(static_cast<double>(angle), &sd, &cd);
-  const float c = static_cast<float>(cd), s = static_cast<float>(sd);  // the f32 rounding first
+  float c = 0.0f, s = 0.0f;
+  bool settled = false;
+  if (fabsf(angle) < 262144.0f) {
+    cos_sin_f32(angle, c, s);
+    settled = bf16_rounding_settled(c, kTrigSettle) && bf16_rounding_settled(s, kTrigSettle);
+  }
+  if (!settled) {
+    double sd, cd;
+    if (fabsf(angle) < 262144.0f)
+      cos_sin_small_angle(angle, cd, sd);
+    else
+      sincos(static_cast<double>(angle), &sd, &cd);
+    c = static_cast<float>(cd);  // the f32 rounding first
+    s = static_cast<float>(sd);
+  }
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t v;
   v[0] = static_cast<__bf16>(c);
