@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the QSA indexer hot path on one MI355X.
 
-One step = qsa_pool_keys (every block) -> qsa_prep_queries (every row) ->
-qsa_score_prepped (every row) -> qsa_select_mask_ws (every row; few long
-rows split over workgroups through a workspace allocated once) over one batch
-of a seeded synthetic workload,
-inputs resident in HBM.  W untimed warm-up steps, then K timed steps between
+One step = qsa_pool_prep (the pool of every block and the prep of every
+query row, one launch) -> qsa_score_prepped (every row) -> qsa_select_mask_ws
+(every row; few long rows split over workgroups through a workspace
+allocated once) over one batch of a seeded synthetic workload, inputs
+resident in HBM.  The pool and the prep are also timed alone, as the
+separate qsa_pool_keys and qsa_prep_queries calls.  W untimed warm-up steps, then K timed steps between
 two device synchronisations; per-kernel durations come from HIP events
 recorded on the launch stream around each call.
 
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU-oracle budget for the baseline sample")
     ap.add_argument("--only", default=None,
-                    help="counter pass: run these comma-separated stages (pool,prep,score,select) "
+                    help="counter pass: run these comma-separated stages (pool,prep,pool_prep,score,select) "
                          "--reps times each on --workload, after a plain copy of a known size")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -91,6 +92,12 @@ class Device:
         self.qsa.qsa_prep_queries(self.q, self.pos, self.wq, w["rotary_dim"], w["theta"], w["eps"],
                                   self.T, self.qhat, self.status)
 
+    def pool_prep(self):
+        """The pool and the query prep in one launch (qsa_pool_prep): the step's first kernel."""
+        w = self.w
+        self.qsa.qsa_pool_prep(self.raw, self.wk, self.q, self.pos, self.wq, w["rotary_dim"], w["theta"],
+                               w["eps"], self.pooled, self.qhat, self.status)
+
     def score(self):
         self.qsa.qsa_score_prepped(self.qhat, self.pos, self.pooled, self.T, self.scores, self.cols,
                                    self.status)
@@ -106,6 +113,9 @@ class Device:
     def prep_bytes(self):
         return self.rows * (1024 + 4 + 1024) + 256
 
+    def pool_prep_bytes(self):
+        return self.pool_bytes() + self.prep_bytes()
+
     def score_bytes(self):
         return self.nmax * 256 + self.rows * (1024 + 4) + 4 * self.pairs
 
@@ -116,10 +126,21 @@ class Device:
         return 4 * self.pairs + self.rows * (self.T + 4)
 
 
-def event_steps(d: Device, n: int, warmup: int, torch):
+def step_stages(d: Device):
+    """The step's launches: pool and query prep (one launch), score, select."""
+    return (("pool_prep", d.pool_prep), ("score", d.score), ("select", d.select))
+
+
+def kernel_stages(d: Device):
+    """Every kernel reported: the step's three, and the pool and the prep
+    launched alone (the separate C-ABI calls)."""
+    return (("pool", d.pool), ("prep", d.prep)) + step_stages(d)
+
+
+def event_steps(d: Device, n: int, warmup: int, torch, stages=None):
     """Per-kernel microseconds of `n` steps after `warmup` untimed ones, each
     launch between its own HIP event pair."""
-    stages = (("pool", d.pool), ("prep", d.prep), ("score", d.score), ("select", d.select))
+    stages = step_stages(d) if stages is None else stages
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         for _, fn in stages:
@@ -140,12 +161,12 @@ def time_steps(d: Device, steps: int, warmup: int, torch, probe_steps: int = 50,
     """Warm-up steps; `probe_steps` steps with HIP events around every kernel
     to find the dominant kernel; the `steps` timed steps between device
     synchronisations, with events around the dominant kernel only (an event
-    pair around each of the four launches costs ~28 us of GPU time per step,
-    354 against 326 us; one pair ~5 us); then `profile_steps` steps with
-    events around every kernel for the other kernels' durations.  Returns
-    the timed steps' wall time, the per-kernel durations (the dominant
-    kernel's from the timed steps) and its name."""
-    stages = (("pool", d.pool), ("prep", d.prep), ("score", d.score), ("select", d.select))
+    pair around each launch costs ~5-7 us of GPU time); then `profile_steps`
+    steps with events around every kernel, and the pool and prep alone, for
+    the other kernels' durations.  Returns the timed steps' wall time, the
+    per-kernel durations (the dominant kernel's from the timed steps) and
+    its name."""
+    stages = step_stages(d)
     stream = torch.cuda.current_stream()
     probe = event_steps(d, probe_steps, warmup, torch)
     dom = max(probe, key=lambda n: sum(probe[n]))
@@ -162,7 +183,7 @@ def time_steps(d: Device, steps: int, warmup: int, torch, probe_steps: int = 50,
                 fn()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = event_steps(d, profile_steps, 0, torch)
+    per = event_steps(d, profile_steps, 0, torch, kernel_stages(d))
     per[dom] = [a.elapsed_time(b) * 1e3 for a, b in tev]
     return wall, per, dom
 
@@ -180,7 +201,7 @@ def back_to_back_us(d: Device, torch, reps: int = 20):
     launches: an event pair costs ~4.5 us of GPU time around a single launch)."""
     stream = torch.cuda.current_stream()
     out = {}
-    for name, fn in (("pool", d.pool), ("prep", d.prep), ("score", d.score), ("select", d.select)):
+    for name, fn in kernel_stages(d):
         for _ in range(3):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -203,7 +224,7 @@ def flush_caches(flush):
 
 
 def cold_step_us(d: Device, torch, reps: int = 10):
-    """Whole-step microseconds (pool, prep, score, select back to back) with L2
+    """Whole-step microseconds (pool + prep, score, select back to back) with L2
     and MALL flushed before every step; one HIP event pair around each step,
     so the figure includes the launch gaps and one event pair's GPU overhead
     and is an upper bound on the kernels' cold time."""
@@ -214,8 +235,7 @@ def cold_step_us(d: Device, torch, reps: int = 10):
         flush_caches(flush)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        d.pool()
-        d.prep()
+        d.pool_prep()
         d.score()
         d.select()
         b.record(stream)
@@ -245,8 +265,10 @@ def median(xs):
 def kernel_report(d: Device, per_us):
     mean = {k: sum(v) / len(v) for k, v in per_us.items()}
     rep = {}
-    for name, b in (("pool", d.pool_bytes()), ("prep", d.prep_bytes()), ("score", d.score_bytes()),
-                    ("select", d.select_bytes())):
+    for name, b in (("pool", d.pool_bytes()), ("prep", d.prep_bytes()), ("pool_prep", d.pool_prep_bytes()),
+                    ("score", d.score_bytes()), ("select", d.select_bytes())):
+        if name not in mean:
+            continue
         t = mean[name]
         gbs = b / (t * 1e-6) / 1e9
         rep[name] = {"mean_us": round(t, 3), "median_us": round(median(per_us[name]), 3),
@@ -262,15 +284,29 @@ def kernel_report(d: Device, per_us):
 
 # the sources each stage's kernel is built from: its counters go stale when they change
 STAGE_SOURCES = {
-    "pool": ["pool.hip", "qsa_device.h"],
-    "prep": ["prep.hip", "qsa_device.h"],
+    "pool": ["pool.hip", "pool_body.h", "qsa_device.h", "qsa_rope_math.h"],
+    "prep": ["prep.hip", "prep_body.h", "qsa_device.h", "qsa_rope_math.h"],
+    "pool_prep": ["pool_prep.hip", "pool_body.h", "prep_body.h", "qsa_device.h", "qsa_rope_math.h"],
     "score": ["score.hip", "qsa_device.h"],
     "select": ["select.hip", "select_split.hip", "select_common.h", "qsa_device.h"],
 }
-# kernel-name fragment of each stage in rocprofv3 output (a stage may launch
-# several kernels: the split select launches a chunk and a merge kernel)
-STAGE_KERNELS = {"pool": "pool_kernel", "prep": "prep_kernel", "score": "score_",
-                 "select": "select_"}
+# kernel-name prefix of each stage in rocprofv3 output, matched against the
+# unqualified kernel name (a stage may launch several kernels: the split
+# select launches a chunk and a merge kernel)
+STAGE_KERNELS = {"pool": "pool_kernel", "prep": "prep_kernel", "pool_prep": "pool_prep_kernel",
+                 "score": "score_", "select": "select_"}
+
+
+def kernel_base(name: str) -> str:
+    """Unqualified kernel name without template arguments or parameters."""
+    n = name.replace("void ", "").split("(")[0].split("<")[0]
+    return n.split("::")[-1]
+
+
+def stage_of(name: str, stage: str) -> bool:
+    frag = STAGE_KERNELS[stage]
+    base = kernel_base(name)
+    return base.startswith(frag) if frag.endswith("_") else base == frag
 COPY_BYTES = 512 << 20  # the counter pass's calibration copy
 
 
@@ -303,7 +339,7 @@ def counter_pass(args, torch, qsa, synth):
     times."""
     w = synth.make_workload(args.workload)
     d = Device(w, torch, qsa)
-    d.pool(); d.prep(); d.score(); d.select()
+    d.pool_prep(); d.score(); d.select()
     src = torch.full((COPY_BYTES,), 1, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -311,7 +347,7 @@ def counter_pass(args, torch, qsa, synth):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    fns = {"pool": d.pool, "prep": d.prep, "score": d.score, "select": d.select}
+    fns = {"pool": d.pool, "prep": d.prep, "pool_prep": d.pool_prep, "score": d.score, "select": d.select}
     stages = [s for s in args.only.split(",") if s]
     for st in stages:
         for _ in range(args.reps):
@@ -355,7 +391,7 @@ def traffic_table(fetch_dir: str, write_dir: str, workload: int):
         cal = median([v for v in copies if v >= 0.5 * top])
         factor = COPY_BYTES / cal  # bytes per counter unit
         for st, frag in STAGE_KERNELS.items():
-            names = sorted({k for _, k, _ in rows if frag in k})
+            names = sorted({k for _, k, _ in rows if stage_of(k, st)})
             if not names:
                 continue
             # one launch of the stage: the median dispatch of each of its kernels
@@ -606,21 +642,23 @@ def side_figures(torch, qsa, synth):
                    ("one_row_64k", synth.single_row(3, 65535)),
                    ("one_row_256k", synth.single_row(4, 262143))):
         d = Device(w, torch, qsa)
-        per = event_steps(d, 20, 5, torch)
+        per = event_steps(d, 20, 5, torch, kernel_stages(d))
         rep, mean = kernel_report(d, per)
         b2b = back_to_back_us(d, torch)
         cold, floor = cold_step_us(d, torch)
-        alg = d.pool_bytes() + d.prep_bytes() + d.score_bytes() + d.select_bytes()
+        step = [n for n, _ in step_stages(d)]
+        alg = d.pool_prep_bytes() + d.score_bytes() + d.select_bytes()
         out[key] = {"rows": d.rows, "tokens": d.T, "pairs": d.pairs,
                     "select_mask_us_per_row": round(b2b["select"] / d.rows, 3),
-                    "step_us_events": round(sum(mean.values()), 2),
-                    "step_us_back_to_back": round(sum(b2b.values()), 2),
+                    "step_kernels": step,
+                    "step_us_events": round(sum(mean[n] for n in step), 2),
+                    "step_us_back_to_back": round(sum(b2b[n] for n in step), 2),
                     "step_us_cold": cold,
                     "event_pair_floor_us": floor,
                     "alg_bytes_step": alg,
-                    "hbm_frac_back_to_back": round(alg / (sum(b2b.values()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "hbm_frac_back_to_back": round(alg / (sum(b2b[n] for n in step) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "hbm_frac_cold_step": round(alg / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                    "pairs_per_s": round(d.pairs / (sum(b2b.values()) * 1e-6), 1),
+                    "pairs_per_s": round(d.pairs / (sum(b2b[n] for n in step) * 1e-6), 1),
                     "kernels_back_to_back_us": b2b,
                     "kernels": rep}
         if key != "prefill_4k":  # decode consumers of the selection

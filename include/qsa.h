@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 9
+#define QSA_ABI_VERSION 10
 
 #define QSA_HEADS 4
 #define QSA_HEAD_DIM 128
@@ -139,6 +139,30 @@ int qsa_prep_queries(const uint16_t* q, int64_t q_stride, const int32_t* pos, in
                      const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
                      float rms_eps, int64_t tokens, uint16_t* qhat, int32_t* dev_status,
                      void* stream);
+
+/*
+ * qsa_pool_prep -- qsa_pool_keys and qsa_prep_queries in one launch.
+ *
+ * [SCORE] summary: the scorer's two inputs, the pooled keys and the normed,
+ * roped query heads, are computed independently of each other; a decode step
+ * that needs both (a batch of query rows against a cache whose newest blocks
+ * still need pooling) runs them in one grid instead of two dependent
+ * launches.  The outputs are bit for bit those of the two calls.
+ *
+ *   raw_keys, key_stride, tokens, k_norm_w, first_block, n_blocks, pooled:
+ *               as for qsa_pool_keys.
+ *   q, q_stride, pos, rows, q_norm_w, qhat, dev_status: as for
+ *               qsa_prep_queries (tokens bounds the valid positions).
+ *   rotary_dim, rope_theta, rms_eps: shared by the keys and the queries.
+ * n_blocks = 0 or rows = 0 runs only the other stage.  Refusals: those of
+ * qsa_pool_keys and qsa_prep_queries for their arguments; the pool's
+ * pointers are checked only when n_blocks > 0, the prep's when rows > 0.
+ */
+int qsa_pool_prep(const uint16_t* raw_keys, int64_t key_stride, int64_t tokens,
+                  const uint16_t* k_norm_w, int64_t first_block, int64_t n_blocks, uint16_t* pooled,
+                  const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                  const uint16_t* q_norm_w, uint16_t* qhat, int32_t rotary_dim, float rope_theta,
+                  float rms_eps, int32_t* dev_status, void* stream);
 
 /*
  * qsa_score_prepped -- qsa_score_rows on queries already prepared by
@@ -393,6 +417,15 @@ int qsa_prep_queries_dev(const uint16_t* q, int64_t q_stride, const int32_t* pos
                          const uint16_t* q_norm_w, int32_t rotary_dim, float rope_theta,
                          float rms_eps, const int32_t* dev_tokens, int64_t max_tokens,
                          uint16_t* qhat, int32_t* dev_status, void* stream);
+
+/* qsa_pool_window and qsa_prep_queries_dev in one launch (see qsa_pool_prep):
+ * the last n_blocks complete blocks of the live cache, and the batch's
+ * prepared query heads.  Refusals: those of the two calls. */
+int qsa_pool_prep_dev(const uint16_t* raw_keys, int64_t key_stride, int64_t max_tokens,
+                      const uint16_t* k_norm_w, int64_t n_blocks, uint16_t* pooled, const uint16_t* q,
+                      int64_t q_stride, const int32_t* pos, int64_t rows, const uint16_t* q_norm_w,
+                      uint16_t* qhat, int32_t rotary_dim, float rope_theta, float rms_eps,
+                      const int32_t* dev_tokens, int32_t* dev_status, void* stream);
 
 /* qsa_score_prepped with the live cache length on the device; score_cols >=
  * max_tokens / 4.  Workgroups past a batch's longest visible prefix exit. */

@@ -19,13 +19,13 @@ from ._lib import (EXPORTS, HEAD_DIM, HEADS, MAX_KEEP_BLOCKS, MAX_TOKENS, RATIO,
                    abi_version, load,
                    strerror)
 
-__all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
+__all__ = ["qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_pool_prep", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_select_mask_noalloc", "qsa_score_select_workspace_bytes",
            "qsa_score_select_flags_offset",
            "qsa_score_select_mask",
-           "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
-           "qsa_select_indices_dev", "qsa_select_indices_ws",
+           "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_pool_prep_dev",
+           "qsa_score_prepped_dev", "qsa_select_indices_dev", "qsa_select_indices_ws",
            "qsa_rope_inv_freq",
            "check_status", "load", "abi_version", "strerror", "QsaError"]
 
@@ -85,6 +85,45 @@ def qsa_pool_keys(raw_keys: torch.Tensor, k_norm_w: torch.Tensor, rotary_dim: in
     _check(lib.qsa_pool_keys(_ptr(raw_keys), key_stride, tokens, _ptr(k_norm_w), rotary_dim,
                              rope_theta, rms_eps, first_block, n_blocks, _ptr(pooled),
                              _stream_ptr(stream)), "qsa_pool_keys")
+
+
+def _pool_prep_args(raw_keys, k_norm_w, q, pos, q_norm_w, pooled, qhat, dev_status):
+    """Shared checks of the combined pool + prep calls; returns (key_stride,
+    q_stride, tokens, rows)."""
+    for t, name in ((raw_keys, "raw_keys"), (k_norm_w, "k_norm_w"), (pooled, "pooled"), (q, "q"),
+                    (q_norm_w, "q_norm_w"), (qhat, "qhat")):
+        _dev(t, name, _BF16_LIKE)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(dev_status, "dev_status", (torch.int32,))
+    key_stride = _rows_2d(raw_keys, "raw_keys", HEAD_DIM)
+    q_stride = _rows_2d(q, "q", HEADS * HEAD_DIM)
+    tokens, rows = raw_keys.shape[0], q.shape[0]
+    _need(k_norm_w.numel() == HEAD_DIM and k_norm_w.is_contiguous(), "k_norm_w must hold 128 values")
+    _need(q_norm_w.numel() == HEAD_DIM and q_norm_w.is_contiguous(), "q_norm_w must hold 128 values")
+    _need(pooled.is_contiguous() and pooled.dim() == 2 and pooled.shape[1] == HEAD_DIM
+          and pooled.shape[0] >= tokens // RATIO, "pooled must be contiguous [tokens/4, 128]")
+    _need(pos.is_contiguous() and pos.numel() == rows, "pos must be contiguous [rows]")
+    _need(qhat.is_contiguous() and qhat.numel() >= rows * HEADS * HEAD_DIM,
+          "qhat must be contiguous [rows, 4, 128]")
+    _need(dev_status.numel() >= 1, "dev_status needs one int32")
+    return key_stride, q_stride, tokens, rows
+
+
+def qsa_pool_prep(raw_keys: torch.Tensor, k_norm_w: torch.Tensor, q: torch.Tensor, pos: torch.Tensor,
+                  q_norm_w: torch.Tensor, rotary_dim: int, rope_theta: float, rms_eps: float,
+                  pooled: torch.Tensor, qhat: torch.Tensor, dev_status: torch.Tensor,
+                  first_block: int = 0, n_blocks: int | None = None, stream=None) -> None:
+    """qsa_pool_keys (blocks [first_block, first_block + n_blocks) of raw_keys)
+    and qsa_prep_queries (q at pos, valid below raw_keys' row count) in one launch."""
+    key_stride, q_stride, tokens, rows = _pool_prep_args(raw_keys, k_norm_w, q, pos, q_norm_w, pooled,
+                                                         qhat, dev_status)
+    if n_blocks is None:
+        n_blocks = tokens // RATIO - first_block
+    lib = load()
+    _check(lib.qsa_pool_prep(_ptr(raw_keys), key_stride, tokens, _ptr(k_norm_w), first_block, n_blocks,
+                             _ptr(pooled), _ptr(q), q_stride, _ptr(pos), rows, _ptr(q_norm_w), _ptr(qhat),
+                             rotary_dim, rope_theta, rms_eps, _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_pool_prep")
 
 
 def qsa_score_rows(q: torch.Tensor, pos: torch.Tensor, q_norm_w: torch.Tensor, rotary_dim: int,
@@ -354,6 +393,22 @@ def qsa_pool_window(raw_keys: torch.Tensor, k_norm_w: torch.Tensor, rotary_dim: 
     _check(lib.qsa_pool_window(_ptr(raw_keys), key_stride, max_tokens, _ptr(k_norm_w), rotary_dim, rope_theta,
                                rms_eps, _ptr(dev_tokens), n_blocks, _ptr(pooled), _ptr(dev_status),
                                _stream_ptr(stream)), "qsa_pool_window")
+
+
+def qsa_pool_prep_dev(raw_keys: torch.Tensor, k_norm_w: torch.Tensor, q: torch.Tensor, pos: torch.Tensor,
+                      q_norm_w: torch.Tensor, rotary_dim: int, rope_theta: float, rms_eps: float,
+                      dev_tokens: torch.Tensor, n_blocks: int, pooled: torch.Tensor, qhat: torch.Tensor,
+                      dev_status: torch.Tensor, stream=None) -> None:
+    """qsa_pool_window and qsa_prep_queries_dev in one launch; raw_keys' row
+    count is the ceiling max_tokens."""
+    key_stride, q_stride, max_tokens, rows = _pool_prep_args(raw_keys, k_norm_w, q, pos, q_norm_w, pooled,
+                                                             qhat, dev_status)
+    _dev_tokens(dev_tokens)
+    lib = load()
+    _check(lib.qsa_pool_prep_dev(_ptr(raw_keys), key_stride, max_tokens, _ptr(k_norm_w), n_blocks, _ptr(pooled),
+                                 _ptr(q), q_stride, _ptr(pos), rows, _ptr(q_norm_w), _ptr(qhat), rotary_dim,
+                                 rope_theta, rms_eps, _ptr(dev_tokens), _ptr(dev_status), _stream_ptr(stream)),
+           "qsa_pool_prep_dev")
 
 
 def qsa_prep_queries_dev(q: torch.Tensor, pos: torch.Tensor, q_norm_w: torch.Tensor, rotary_dim: int,

@@ -33,15 +33,15 @@ MAX_TOKENS = 262147
 NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Every symbol the header declares.
-EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_score_prepped",
+EXPORTS = ("qsa_pool_keys", "qsa_score_rows", "qsa_prep_queries", "qsa_pool_prep", "qsa_score_prepped",
            "qsa_select_mask", "qsa_select_indices", "qsa_select_workspace_bytes",
            "qsa_select_mask_ws", "qsa_select_mask_noalloc", "qsa_score_select_workspace_bytes",
            "qsa_score_select_flags_offset",
            "qsa_score_select_mask",
-           "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_score_prepped_dev",
-           "qsa_select_indices_dev", "qsa_select_indices_ws", "qsa_rope_inv_freq", "qsa_strerror",
+           "qsa_gather_kv", "qsa_pool_window", "qsa_prep_queries_dev", "qsa_pool_prep_dev",
+           "qsa_score_prepped_dev", "qsa_select_indices_dev", "qsa_select_indices_ws", "qsa_rope_inv_freq", "qsa_strerror",
            "qsa_abi_version")
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _lib = None
 
@@ -68,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_score_rows.restype = ctypes.c_int
     lib.qsa_prep_queries.argtypes = [P, I64, P, I64, P, I32, F, F, I64, P, P, P]
     lib.qsa_prep_queries.restype = ctypes.c_int
+    lib.qsa_pool_prep.argtypes = [P, I64, I64, P, I64, I64, P, P, I64, P, I64, P, P, I32, F, F, P, P]
+    lib.qsa_pool_prep.restype = ctypes.c_int
     lib.qsa_score_prepped.argtypes = [P, P, I64, P, I64, P, I64, I64, P, P]
     lib.qsa_score_prepped.restype = ctypes.c_int
     lib.qsa_select_mask.argtypes = [P, I64, I64, P, I64, I64, I64, P, P, P]
@@ -95,6 +97,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_pool_window.restype = ctypes.c_int
     lib.qsa_prep_queries_dev.argtypes = [P, I64, P, I64, P, I32, F32, F32, P, I64, P, P, P]
     lib.qsa_prep_queries_dev.restype = ctypes.c_int
+    lib.qsa_pool_prep_dev.argtypes = [P, I64, I64, P, I64, P, P, I64, P, I64, P, P, I32, F32, F32, P, P, P]
+    lib.qsa_pool_prep_dev.restype = ctypes.c_int
     lib.qsa_score_prepped_dev.argtypes = [P, P, I64, P, P, I64, P, I64, I64, P, P]
     lib.qsa_score_prepped_dev.restype = ctypes.c_int
     lib.qsa_select_indices_dev.argtypes = [P, I64, I64, P, I64, P, I64, I64, P, I64, P, P, P, I64, P]

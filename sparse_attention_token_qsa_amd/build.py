@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
-SOURCES = ["qsa_abi.hip", "pool.hip", "prep.hip", "score.hip", "select.hip", "select_split.hip", "fused.hip", "gather.hip"]
+SOURCES = ["qsa_abi.hip", "pool.hip", "prep.hip", "pool_prep.hip", "score.hip", "select.hip", "select_split.hip", "fused.hip", "gather.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

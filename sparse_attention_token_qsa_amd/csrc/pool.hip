@@ -1,207 +1,12 @@
-// Block pooling: every complete 4-token block's raw keys -> one pooled key.
-//
-// pegainfer pull request 1160 ("score QSA token-indexer blocks in native
-// CUDA"), summary: the block's raw keys are averaged in float32 and cast back
-// to bf16, then (1 + w) RMSNorm and partial RoPE at the block's first token.
-//
-// Layout: a workgroup of 256 threads pools 16 consecutive blocks; each block
-// is owned by 16 lanes (of one wave) holding 8 channels each, so one block's
-// four 256-byte token rows are read as four 16-byte loads per lane and the
-// pooled 256-byte row leaves as one 16-byte store per lane.  The loads are
-// issued first; each lane's cos/sin (for the rotary pairs g, g + 16, ... it
-// rotates) overlap them.  The RMSNorm statistic is a 16-lane DPP reduction
-// in double.  The RoPE goes pair by pair through the block's row in LDS, so
-// every lane rotates (two pairs each at rotary_dim 64) and any even
-// rotary_dim works; a block's lanes share a wave, so wave-level ordering of
-// the LDS traffic suffices.  Roundings to bf16 use the hardware's
-// round-to-nearest-even conversion; a NaN result is written as 0x7FC0.  The
-// stage is HBM-bound: 1 KiB read and 256 B written per block.
-#include "qsa_device.h"
-#include "qsa_launch.h"
+// Block pooling launch: one workgroup per 16 consecutive blocks (pool_body.h).
+#include "pool_body.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kPoolThreads = 256;
-constexpr int kPoolBlocksPerGroup = kPoolThreads / 16;
-
-struct PoolArgs {
-  const uint16_t* raw;
-  int64_t key_stride;
-  const uint16_t* w;
-  uint16_t* pooled;
-  int64_t first_block;
-  int64_t n_blocks;
-  RopeParams rp;
-  // window mode (dev_tokens set): the last n_blocks complete blocks of a
-  // cache of *dev_tokens tokens (at most `ceiling`), first_block unused
-  const int32_t* dev_tokens;
-  int64_t ceiling;
-  int32_t* status;
-};
-
-__device__ __forceinline__ void unpack8(const uint4 u, float (&v)[8]) {
-  const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(wd[i] << 16);
-    v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
-  }
-}
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t v;
-  v[0] = static_cast<__bf16>(lo);
-  v[1] = static_cast<__bf16>(hi);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// bf16 NaN test of both halves of a packed word: a half is NaN exactly when
-// its magnitude bits exceed 0x7F80, i.e. reach 0x8000 after adding 0x7F
-// (no carry crosses into the other half).
-__device__ __forceinline__ uint32_t nan_halves(uint32_t d) {
-  return ((d & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u;
-}
-
 template <bool kVec>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
-  // one 128-channel bf16 row per block slot: the normed key, then (in place)
-  // the rotated channels
-  __shared__ __attribute__((aligned(16))) uint16_t ys[kPoolBlocksPerGroup][kHeadDim];
-
-  const int tid = threadIdx.x;
-  const int slot = tid >> 4;  // block slot within the group (16 lanes of one wave)
-  const int g = tid & 15;     // channel group: channels 8g .. 8g+7
-  const int64_t group_first = static_cast<int64_t>(blockIdx.x) * kPoolBlocksPerGroup;
-  const int64_t blk = group_first + slot;
-  int64_t first = a.first_block, count = a.n_blocks;
-  if (a.dev_tokens != nullptr) {
-    const int64_t complete = live_tokens(a.ceiling, a.dev_tokens, a.status) / kRatio;
-    first = complete > a.n_blocks ? complete - a.n_blocks : 0;
-    count = complete - first;
-  }
-  const bool live = blk < count;
-  const int64_t b = first + blk;
-
-  // raw keys first: four 16-byte token rows per lane
-  uint4 v[4];
-  if (live) {
-    const uint16_t* base = a.raw + kRatio * b * a.key_stride + 8 * g;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint16_t* src = base + t * a.key_stride;
-      if constexpr (kVec) {
-        v[t] = *reinterpret_cast<const uint4*>(src);
-      } else {
-        v[t].x = src[0] | (static_cast<uint32_t>(src[1]) << 16);
-        v[t].y = src[2] | (static_cast<uint32_t>(src[3]) << 16);
-        v[t].z = src[4] | (static_cast<uint32_t>(src[5]) << 16);
-        v[t].w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  double wp[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) wp[e] = 1.0 + static_cast<double>(bf16_to_f32(a.w[8 * g + e]));
-
-  // cos/sin at the anchor 4b for the rotary pairs this lane rotates: pairs
-  // i = g, g + 16, g + 32, g + 48 below rotary_dim / 2 (computed while the
-  // loads are in flight)
-  const int rd = a.rp.rotary_dim;
-  const int half = rd >> 1;
-  const int64_t anchor = kRatio * b;
-  uint32_t cs[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = g + 16 * k;
-    cs[k] = i < half ? rope_cos_sin_bf16x2(anchor, a.rp.inv_freq[i]) : 0u;
-  }
-
-  // f32 mean of the 4 tokens in token order, cast to bf16.
-  float k0[8], k1[8], k2[8], k3[8], m[8];
-  unpack8(v[0], k0);
-  unpack8(v[1], k1);
-  unpack8(v[2], k2);
-  unpack8(v[3], k3);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma clang fp contract(off)
-    float s = k0[e] + k1[e];
-    s = s + k2[e];
-    s = s + k3[e];
-    m[e] = rb_hw(s * 0.25f);
-  }
-
-  // (1 + w) RMSNorm in double, rounded to f32 and then to bf16.
-  double ss = 0.0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss += static_cast<double>(m[e]) * static_cast<double>(m[e]);
-  const double r = inv_rms(row16_sum(ss), a.rp.eps);
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma clang fp contract(off)
-    y[e] = rb_hw(static_cast<float>((static_cast<double>(m[e]) * r) * wp[e]));
-  }
-  uint16_t* row = &ys[slot][0];
-  *reinterpret_cast<uint4*>(row + 8 * g) =
-      make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
-  wave_lds_sync();  // a block's 16 lanes live in one wave
-
-  // Partial RoPE at the block's first token, pair by pair: every product and
-  // sum rounds to bf16, o_i = rb(rb(y_i c) - rb(y_{i+h} s)),
-  // o_{i+h} = rb(rb(y_{i+h} c) + rb(y_i s)).  All of the row is read before
-  // any rotated channel is written back in its place.
-  float x0[4], x1[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = g + 16 * k;
-    x0[k] = i < half ? bf16_to_f32(row[i]) : 0.0f;
-    x1[k] = i < half ? bf16_to_f32(row[i + half]) : 0.0f;
-  }
-  wave_lds_sync();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-#pragma clang fp contract(off)
-    const int i = g + 16 * k;
-    if (i < half) {
-      const float c = __uint_as_float(cs[k] << 16);
-      const float sn = __uint_as_float(cs[k] & 0xFFFF0000u);
-      const float o0 = rb_hw(x0[k] * c) - rb_hw(x1[k] * sn);
-      const float o1 = rb_hw(x1[k] * c) + rb_hw(x0[k] * sn);
-      row[i] = static_cast<uint16_t>(pack2(o0, 0.0f) & 0xFFFFu);
-      row[i + half] = static_cast<uint16_t>(pack2(o1, 0.0f) & 0xFFFFu);
-    }
-  }
-  wave_lds_sync();
-  if (live) {
-    uint4 out = *reinterpret_cast<const uint4*>(row + 8 * g);
-    if (nan_halves(out.x) | nan_halves(out.y) | nan_halves(out.z) | nan_halves(out.w)) {
-      // rare: a non-finite key, weight or norm; NaN is written as 0x7FC0
-      uint32_t wd[4] = {out.x, out.y, out.z, out.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (nan_halves(wd[i]) & 0x8000u) wd[i] = (wd[i] & 0xFFFF0000u) | 0x7FC0u;
-        if (nan_halves(wd[i]) & 0x80000000u) wd[i] = (wd[i] & 0x0000FFFFu) | 0x7FC00000u;
-      }
-      out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    }
-    uint16_t* dst = a.pooled + b * kHeadDim + 8 * g;
-    if constexpr (kVec) {
-      *reinterpret_cast<uint4*>(dst) = out;
-    } else {
-      const uint32_t wd[4] = {out.x, out.y, out.z, out.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dst[2 * i] = static_cast<uint16_t>(wd[i] & 0xFFFFu);
-        dst[2 * i + 1] = static_cast<uint16_t>(wd[i] >> 16);
-      }
-    }
-  }
+  pool_group<kVec>(a, blockIdx.x);
 }
 
 }  // namespace

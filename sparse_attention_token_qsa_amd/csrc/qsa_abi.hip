@@ -28,6 +28,31 @@ void fill_inv_freq(int32_t rotary_dim, float theta, float* out) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
 
+// Refusals of qsa_pool_prep(_dev) past its extents: those of the pool call for
+// its key arguments and of the prep call for its query arguments.  The pool's
+// pointers are needed only when n_blocks > 0, the prep's when rows > 0.
+int check_pool_prep(const uint16_t* raw_keys, int64_t key_stride, int64_t tokens,
+                    const uint16_t* k_norm_w, int64_t n_blocks, const uint16_t* pooled,
+                    const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                    const uint16_t* q_norm_w, const uint16_t* qhat, int32_t rotary_dim,
+                    float rope_theta, float rms_eps, const int32_t* dev_status) {
+  if (key_stride < QSA_HEAD_DIM || q_stride < QSA_HEADS * QSA_HEAD_DIM) return QSA_ERR_STRIDE;
+  const int rc = check_rope(rotary_dim, rope_theta, rms_eps);
+  if (rc != QSA_OK) return rc;
+  if (tokens > QSA_MAX_TOKENS || rows > INT32_MAX) return QSA_ERR_CAPACITY;
+  int64_t need;
+  if (n_blocks > 0) {
+    if (raw_keys == nullptr || k_norm_w == nullptr || pooled == nullptr) return QSA_ERR_NULL;
+    if (mul_overflows(tokens, key_stride, &need)) return QSA_ERR_CAPACITY;
+  }
+  if (rows > 0) {
+    if (q == nullptr || pos == nullptr || q_norm_w == nullptr || qhat == nullptr || dev_status == nullptr)
+      return QSA_ERR_NULL;
+    if (mul_overflows(rows, q_stride, &need)) return QSA_ERR_CAPACITY;
+  }
+  return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +152,27 @@ int qsa_prep_queries(const uint16_t* q, int64_t q_stride, const int32_t* pos, in
   fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
   return launch_status(qsa::launch_prep(q, q_stride, pos, rows, q_norm_w, rp, tokens, qhat,
                                         dev_status, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_pool_prep(const uint16_t* raw_keys, int64_t key_stride, int64_t tokens,
+                  const uint16_t* k_norm_w, int64_t first_block, int64_t n_blocks, uint16_t* pooled,
+                  const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                  const uint16_t* q_norm_w, uint16_t* qhat, int32_t rotary_dim, float rope_theta,
+                  float rms_eps, int32_t* dev_status, void* stream) {
+  if (tokens < 0 || first_block < 0 || n_blocks < 0 || rows < 0) return QSA_ERR_EXTENT;
+  if (first_block > tokens / QSA_RATIO || n_blocks > tokens / QSA_RATIO - first_block)
+    return QSA_ERR_EXTENT;
+  const int rc = check_pool_prep(raw_keys, key_stride, tokens, k_norm_w, n_blocks, pooled, q, q_stride,
+                                 pos, rows, q_norm_w, qhat, rotary_dim, rope_theta, rms_eps, dev_status);
+  if (rc != QSA_OK) return rc;
+  if (n_blocks == 0 && rows == 0) return QSA_OK;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_pool_prep(raw_keys, key_stride, k_norm_w, first_block, n_blocks, pooled,
+                                             q, q_stride, pos, rows, q_norm_w, qhat, rp, tokens,
+                                             dev_status, static_cast<hipStream_t>(stream)));
 }
 
 int qsa_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
@@ -355,6 +401,27 @@ int qsa_prep_queries_dev(const uint16_t* q, int64_t q_stride, const int32_t* pos
   fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
   return launch_status(qsa::launch_prep(q, q_stride, pos, rows, q_norm_w, rp, max_tokens, qhat, dev_status,
                                         static_cast<hipStream_t>(stream), dev_tokens));
+}
+
+int qsa_pool_prep_dev(const uint16_t* raw_keys, int64_t key_stride, int64_t max_tokens,
+                      const uint16_t* k_norm_w, int64_t n_blocks, uint16_t* pooled, const uint16_t* q,
+                      int64_t q_stride, const int32_t* pos, int64_t rows, const uint16_t* q_norm_w,
+                      uint16_t* qhat, int32_t rotary_dim, float rope_theta, float rms_eps,
+                      const int32_t* dev_tokens, int32_t* dev_status, void* stream) {
+  if (max_tokens < 0 || n_blocks < 0 || rows < 0) return QSA_ERR_EXTENT;
+  if (n_blocks > max_tokens / QSA_RATIO) return QSA_ERR_EXTENT;
+  const int rc = check_pool_prep(raw_keys, key_stride, max_tokens, k_norm_w, n_blocks, pooled, q, q_stride,
+                                 pos, rows, q_norm_w, qhat, rotary_dim, rope_theta, rms_eps, dev_status);
+  if (rc != QSA_OK) return rc;
+  if (n_blocks == 0 && rows == 0) return QSA_OK;
+  if (dev_tokens == nullptr || dev_status == nullptr) return QSA_ERR_NULL;
+  qsa::RopeParams rp{};
+  rp.rotary_dim = rotary_dim;
+  rp.eps = rms_eps;
+  fill_inv_freq(rotary_dim, rope_theta, rp.inv_freq);
+  return launch_status(qsa::launch_pool_prep(raw_keys, key_stride, k_norm_w, 0, n_blocks, pooled, q,
+                                             q_stride, pos, rows, q_norm_w, qhat, rp, max_tokens,
+                                             dev_status, static_cast<hipStream_t>(stream), dev_tokens));
 }
 
 int qsa_score_prepped_dev(const uint16_t* qhat, const int32_t* pos, int64_t rows,

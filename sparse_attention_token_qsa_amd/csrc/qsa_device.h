@@ -63,6 +63,16 @@ __device__ __forceinline__ float score_fast(float h0, float h1, float h2, float 
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Eight packed bf16 (element 2i in the low half of word i) -> floats (exact).
+__device__ __forceinline__ void unpack_bf16x8(const uint4 u, float (&v)[8]) {
+  const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(wd[i] << 16);
+    v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+  }
+}
+
 // float -> bf16 bit pattern, round to nearest even; NaN -> 0x7FC0.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

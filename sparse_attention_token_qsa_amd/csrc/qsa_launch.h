@@ -31,6 +31,16 @@ hipError_t launch_prep(const uint16_t* q, int64_t q_stride, const int32_t* pos, 
                        const uint16_t* w, const RopeParams& rp, int64_t tokens, uint16_t* qhat,
                        int32_t* status, hipStream_t stream, const int32_t* dev_tokens = nullptr);
 
+// The pool of a block range and the prep of a batch of query rows in one
+// launch (pool_prep.hip).  With dev_tokens set, the pool takes the last
+// n_blocks complete blocks of the live cache (first_block unused) and
+// `tokens` is the ceiling, as for launch_pool and launch_prep.
+hipError_t launch_pool_prep(const uint16_t* raw, int64_t key_stride, const uint16_t* wk,
+                            int64_t first_block, int64_t n_blocks, uint16_t* pooled,
+                            const uint16_t* q, int64_t q_stride, const int32_t* pos, int64_t rows,
+                            const uint16_t* wq, uint16_t* qhat, const RopeParams& rp, int64_t tokens,
+                            int32_t* status, hipStream_t stream, const int32_t* dev_tokens = nullptr);
+
 hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows,
                                 const uint16_t* pooled, int64_t tokens, float* scores,
                                 int64_t score_cols, int32_t* status, hipStream_t stream,

@@ -82,15 +82,6 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
   return o;
 }
 
-__device__ __forceinline__ void unpack_bf16x8(const uint4 u, float (&v)[8]) {
-  const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_to_f32(wd[i] & 0xFFFFu);
-    v[2 * i + 1] = bf16_to_f32(wd[i] >> 16);
-  }
-}
-
 // Workgroup geometry.
 template <int WM, int MS, int D, bool PREP>
 struct ScoreGeom {
@@ -184,20 +175,56 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
 #pragma unroll
   for (int e = 0; e < 8; ++e) wv[e] = PREP ? 0.0f : bf16_to_f32(a.w[8 * g + e]);
 
-  // ---- positions and visible block counts (wave 0)
+  // ---- key ring loads.  Wave w loads rows [4 (w kL + i), +4) of a tile, i < kL:
+  // lane L of load i fills LDS bytes 1024 (w kL + i) + 16 L, i.e. row
+  // 4 (w kL + i) + L / 16 at chunk L % 16, which holds the key's chunk
+  // (L % 16) ^ (row & 7).  Block indices are clamped to `last`, so loads
+  // never leave the pooled buffer and every step issues the same number of
+  // loads.
+  constexpr int kL = G::kLoads;
+  const int lrow = lane >> 4;
+  const int lchunk = lane & 15;
+  auto load_tile = [&](int nb0, int stage, int last) {
+#pragma unroll
+    for (int i = 0; i < kL; ++i) {
+      const int row = 4 * (wave * kL + i) + lrow;
+      const int blk = min(nb0 + row, last);
+      const uint16_t* src = a.pooled + static_cast<int64_t>(blk) * kHeadDim + 8 * (lchunk ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       static_cast<void*>(smem + stage * G::kStageBytes + 1024 * (wave * kL + i)),
+                                       16, 0, 0);
+    }
+  };
+
+  // ---- positions and visible block counts (wave 0).  With prepared queries
+  // the LDS is free from the start, so the first D - 1 tiles are requested
+  // right behind the positions, clamped to the pooled buffer's last block
+  // instead of the batch's last visible one: the two latencies overlap.  A
+  // tile row past every row's prefix feeds only scores that are never stored.
+  const int nb_cap = static_cast<int>(a.tokens / kRatio);
+  int prow = 0;       // this lane's row position (wave 0)
+  int64_t live = 0;   // the live cache length it must lie below
+  if (wave == 0 && lane < RG && row0 + lane < a.rows) {
+    prow = a.pos[row0 + lane];
+    live = live_tokens(a.tokens, a.dev_tokens, a.status);
+  }
+  if constexpr (PREP) {
+    if (nb_cap > 0)  // uniform
+#pragma unroll
+      for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t, nb_cap - 1);
+  }
   if (wave == 0) {
-    int n = 0, p = 0, nlo = 0x7FFFFFFF;
+    int n = 0, nlo = 0x7FFFFFFF;
     if (lane < RG) {
       const int64_t r = row0 + lane;
       if (r < a.rows) {
-        p = a.pos[r];
-        if (p >= 0 && p < live_tokens(a.tokens, a.dev_tokens, a.status))
-          n = (p + 1) / kRatio;
+        if (prow >= 0 && prow < live)
+          n = (prow + 1) / kRatio;
         else if (split == 0)
           atomicOr(a.status, 1);
       }
       nvis[lane] = n;
-      ppos[lane] = p;
+      ppos[lane] = prow;
       nlo = n;
     }
     const uint32_t mx = wave_max_u32(static_cast<uint32_t>(n));
@@ -210,7 +237,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   __syncthreads();
   const int nmax = sh_nmax;
   const int nmin = sh_nmin;  // blocks every row of the workgroup sees
-  if (blk_begin >= nmax) return;  // uniform across the workgroup; nothing in flight to LDS
+  if (blk_begin >= nmax) {  // uniform across the workgroup
+    if constexpr (PREP) wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+    return;
+  }
   const int blk_end = nmax;
 
   if constexpr (!PREP) {
@@ -313,28 +343,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   __syncthreads();  // every wave holds its A fragments: the LDS becomes the key ring
   }
 
-  // ---- key ring.  Wave w loads rows [4 (w kL + i), +4) of a tile, i < kL:
-  // lane L of load i fills LDS bytes 1024 (w kL + i) + 16 L, i.e. row
-  // 4 (w kL + i) + L / 16 at chunk L % 16, which holds the key's chunk
-  // (L % 16) ^ (row & 7).  Block indices are clamped to the last block the
-  // workgroup may use, so loads never leave the cache and every step issues
-  // the same number of loads.
-  constexpr int kL = G::kLoads;
-  const int lrow = lane >> 4;
-  const int lchunk = lane & 15;
-  auto load_tile = [&](int nb0, int stage) {
+  // ---- the first D - 1 tiles (after the prologue, whose LDS they reuse)
+  if constexpr (!PREP) {
 #pragma unroll
-    for (int i = 0; i < kL; ++i) {
-      const int row = 4 * (wave * kL + i) + lrow;
-      const int blk = min(nb0 + row, blk_end - 1);
-      const uint16_t* src = a.pooled + static_cast<int64_t>(blk) * kHeadDim + 8 * (lchunk ^ (row & 7));
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       static_cast<void*>(smem + stage * G::kStageBytes + 1024 * (wave * kL + i)),
-                                       16, 0, 0);
-    }
-  };
-#pragma unroll
-  for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t);
+    for (int t = 0; t < D - 1; ++t) load_tile(blk_begin + t * stride, t, blk_end - 1);
+  }
 
   // per-lane output rows: subtile ms holds rows 8 (MS m + ms) + 2 q4 + (lane >> 5).
   // With BUFST the stores go through a buffer resource over the workgroup's
@@ -375,7 +388,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
   for (int nb0 = blk_begin; nb0 < blk_end; nb0 += stride) {
     int lstage = stage + D - 1;
     lstage = lstage >= D ? lstage - D : lstage;
-    load_tile(nb0 + (D - 1) * stride, lstage);
+    load_tile(nb0 + (D - 1) * stride, lstage, blk_end - 1);
     const unsigned char* sb = smem + stage * G::kStageBytes + brow;
     f32x16_t acc[MS];
 #pragma unroll

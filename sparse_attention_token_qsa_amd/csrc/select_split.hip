@@ -68,7 +68,34 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
   const int chunk = static_cast<int>(blockIdx.x - row * a.chunks);
   const int64_t slot = row * a.chunks + chunk;
   const int64_t p = a.pos[row];
-  if (p < 0 || p >= live_tokens(a.tokens, a.dev_tokens, a.status)) {
+  const int64_t live = live_tokens(a.tokens, a.dev_tokens, a.status);
+  const int b0 = chunk * kSplitChunk;
+  // The chunk's scores are requested before the row's position arrives,
+  // clamped to the buffer's first tokens / 4 columns; the keys below keep
+  // only the visible ones.
+  const float* srow = a.scores + row * a.score_cols + b0;
+  const int ncap = static_cast<int>(min(max(a.tokens / kRatio - b0, static_cast<int64_t>(0)),
+                                        static_cast<int64_t>(kSplitChunk)));
+  float4 v[VEC ? KPT / 4 : 1];
+  float sv[VEC ? 1 : KPT];
+  if (ncap > 0) {  // uniform
+    if constexpr (VEC) {
+      const float4* s4 = reinterpret_cast<const float4*>(srow);
+      const int qcap = (ncap - 1) >> 2;
+#pragma unroll
+      for (int g = 0; g < KPT / 4; ++g) {
+        const int q = tid + g * NT;
+        v[g] = s4[q < qcap ? q : qcap];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int b = tid + j * NT;
+        sv[j] = srow[b < ncap ? b : ncap - 1];
+      }
+    }
+  }
+  if (p < 0 || p >= live) {
     if (tid == 0) {
       if (chunk == 0) atomicOr(a.status, QSA_STATUS_BAD_POSITION);
       a.cnt[slot] = -1;
@@ -76,7 +103,6 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
     return;
   }
   const int n_row = static_cast<int>((p + 1) / kRatio);
-  const int b0 = chunk * kSplitChunk;
   const int n = min(max(n_row - b0, 0), kSplitChunk);  // this chunk's visible blocks
   if (n == 0) {
     if (tid == 0) a.cnt[slot] = 0;
@@ -87,40 +113,25 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
 
   auto blk = [&](int j) { return VEC ? 4 * (tid + (j >> 2) * NT) + (j & 3) : tid + j * NT; };
 
-  const float* srow = a.scores + row * a.score_cols + b0;
   uint32_t key[KPT];
   int bad = 0;
   if constexpr (VEC) {
-    const float4* s4 = reinterpret_cast<const float4*>(srow);
-    const int qlast = (n - 1) >> 2;
-    float4 v[KPT / 4];
-#pragma unroll
-    for (int g = 0; g < KPT / 4; ++g) {
-      const int q = tid + g * NT;
-      v[g] = s4[q < qlast ? q : qlast];
-    }
 #pragma unroll
     for (int g = 0; g < KPT / 4; ++g) {
       const float e[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool live = blk(4 * g + i) < n;
-        bad |= live && !is_finite_bits(e[i]);
-        key[4 * g + i] = live ? score_key(e[i]) : 0u;
+        const bool vis = blk(4 * g + i) < n;
+        bad |= vis && !is_finite_bits(e[i]);
+        key[4 * g + i] = vis ? score_key(e[i]) : 0u;
       }
     }
   } else {
-    float sv[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int b = blk(j);
-      sv[j] = srow[b < n ? b : n - 1];
-    }
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool live = blk(j) < n;
-      bad |= live && !is_finite_bits(sv[j]);
-      key[j] = live ? score_key(sv[j]) : 0u;
+      const bool vis = blk(j) < n;
+      bad |= vis && !is_finite_bits(sv[j]);
+      key[j] = vis ? score_key(sv[j]) : 0u;
     }
   }
   if (tid < 256) hist[tid] = 0u;
@@ -283,6 +294,7 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
   const int64_t t_begin = static_cast<int64_t>(slice) * kSliceTokens;
   const int64_t t_end = min(t_begin + kSliceTokens, T);
   const int64_t p = a.pos[row];
+  const int64_t live = live_tokens(T, a.dev_tokens, nullptr);
 
   // this slice's bytes: block bytes from keptbits (kept = 1), the rest 1 for
   // t <= last, 0 otherwise
@@ -333,15 +345,11 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
     }
   };
 
-  if (p < 0 || p >= live_tokens(T, a.dev_tokens, nullptr)) {
-    write_slice(0, -1, false);
-    return;
-  }
-  const int n = static_cast<int>((p + 1) / kRatio);
-  // The union's slots, loaded before the counts arrive: every chunk before
-  // the row's last visible one is full (4096 >= keep blocks) and emitted
-  // exactly keep composites, so slot i is entry i % keep of chunk i / keep;
-  // slots past the emitted total are cleared once the counts are known.
+  // The union's slots, loaded before the position and the counts arrive:
+  // every chunk before the row's last visible one is full (4096 >= keep
+  // blocks) and emitted exactly keep composites, so slot i is entry i % keep
+  // of chunk i / keep; slots past the emitted total are cleared once the
+  // counts are known.
   const int keep = a.keep_max;
   const uint64_t* base = a.cand + row * a.chunks * kMaxKeep;
   uint64_t cv[KPT];
@@ -351,7 +359,13 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
     const int c = i / keep;
     cv[j] = c < a.chunks ? base[static_cast<int64_t>(c) * kMaxKeep + (i - c * keep)] : 0ull;
   }
-  if (tid < a.chunks) cnts[tid] = a.cnt[row * a.chunks + tid];
+  const int mycnt = tid < a.chunks ? a.cnt[row * a.chunks + tid] : 0;
+  if (p < 0 || p >= live) {
+    write_slice(0, -1, false);
+    return;
+  }
+  const int n = static_cast<int>((p + 1) / kRatio);
+  if (tid < a.chunks) cnts[tid] = mycnt;
   if (tid < 64) kcount[tid] = 0;
   if (tid < kSplitChunk / 32) keptbits[tid] = 0u;
   if (tid < 256) hist[tid] = 0u;

@@ -64,6 +64,24 @@ hipError_t launch_prep(const uint16_t* q, int64_t q_stride, const int32_t* pos, 
   return hipSuccess;
 }
 
+hipError_t launch_pool_prep(const uint16_t* raw, int64_t key_stride, const uint16_t* wk, int64_t first_block,
+                            int64_t n_blocks, uint16_t* pooled, const uint16_t* q, int64_t q_stride,
+                            const int32_t* pos, int64_t rows, const uint16_t* wq, uint16_t* qhat,
+                            const RopeParams& rp, int64_t tokens, int32_t* status, hipStream_t,
+                            const int32_t* dev_tokens) {
+  REQUIRE(n_blocks >= 0 && rows >= 0 && rows <= INT32_MAX && (n_blocks > 0 || rows > 0));
+  REQUIRE(tokens >= 0 && tokens <= QSA_MAX_TOKENS);
+  if (n_blocks > 0) {
+    REQUIRE(raw && wk && pooled && key_stride >= 128 && first_block >= 0);
+    REQUIRE(dev_tokens ? n_blocks <= tokens / 4 : first_block + n_blocks <= tokens / 4);
+  }
+  if (rows > 0) REQUIRE(q && pos && wq && qhat && status && q_stride >= 512);
+  if (dev_tokens) REQUIRE(status);
+  check_rope(rp);
+  ++g_launches;
+  return hipSuccess;
+}
+
 hipError_t launch_score_prepped(const uint16_t* qhat, const int32_t* pos, int64_t rows, const uint16_t*,
                                 int64_t tokens, float*, int64_t score_cols, int32_t* status, hipStream_t,
                                 const int32_t*) {
@@ -237,12 +255,36 @@ int main() {
   const long l0 = g_launches;
   REQUIRE(qsa_pool_keys(u, 128, 64, u, 64, 1e4f, 1e-6f, 0, 16, (uint16_t*)F, nullptr) == QSA_OK);
   REQUIRE(g_launches == l0 + 1);
+  // the combined pool + prep: either stage alone, neither, and each stage's refusals
+  {
+    int32_t* i32 = static_cast<int32_t*>(F);
+    uint16_t* w16 = static_cast<uint16_t*>(F);
+    const long l1 = g_launches;
+    REQUIRE(qsa_pool_prep(u, 128, 64, u, 0, 16, w16, u, 512, i32, 4, u, w16, 64, 1e4f, 1e-6f, i32, nullptr) == QSA_OK);
+    REQUIRE(qsa_pool_prep(nullptr, 128, 64, nullptr, 0, 0, nullptr, u, 512, i32, 4, u, w16, 64, 1e4f, 1e-6f, i32,
+                          nullptr) == QSA_OK);
+    REQUIRE(qsa_pool_prep(u, 128, 64, u, 0, 16, w16, nullptr, 512, nullptr, 0, nullptr, nullptr, 64, 1e4f, 1e-6f,
+                          nullptr, nullptr) == QSA_OK);
+    REQUIRE(qsa_pool_prep(u, 128, 64, u, 0, 0, w16, u, 512, i32, 0, u, w16, 64, 1e4f, 1e-6f, i32, nullptr) == QSA_OK);
+    REQUIRE(g_launches == l1 + 3);
+    REQUIRE(qsa_pool_prep(u, 128, 64, u, 0, 16, w16, u, 511, i32, 4, u, w16, 64, 1e4f, 1e-6f, i32, nullptr) ==
+            QSA_ERR_STRIDE);
+    REQUIRE(qsa_pool_prep(u, 128, 64, u, 1, 16, w16, u, 512, i32, 4, u, w16, 64, 1e4f, 1e-6f, i32, nullptr) ==
+            QSA_ERR_EXTENT);
+    REQUIRE(qsa_pool_prep(u, 128, 64, u, 0, 16, w16, u, 512, i32, 4, u, w16, 64, 1e4f, 1e-6f, nullptr, nullptr) ==
+            QSA_ERR_NULL);
+    REQUIRE(qsa_pool_prep_dev(u, 128, 64, u, 1, w16, u, 512, i32, 4, u, w16, 64, 1e4f, 1e-6f, nullptr, i32,
+                              nullptr) == QSA_ERR_NULL);
+    REQUIRE(qsa_pool_prep_dev(u, 128, 64, u, 17, w16, u, 512, i32, 4, u, w16, 64, 1e4f, 1e-6f, i32, i32,
+                              nullptr) == QSA_ERR_EXTENT);
+    REQUIRE(g_launches == l1 + 3);
+  }
   // the no-allocation select: its scratch limit, then an accepted split call
   REQUIRE(qsa_select_mask_noalloc((float*)F, 65536, 128 * 65536, (int32_t*)F, 128, 262144, 2048, (uint8_t*)F,
                                   (int32_t*)F, nullptr) == QSA_ERR_CAPACITY);
   REQUIRE(qsa_select_mask_noalloc((float*)F, 65536, 16 * 65536, (int32_t*)F, 16, 262144, 2048, (uint8_t*)F,
                                   (int32_t*)F, nullptr) == QSA_OK);
-  REQUIRE(g_launches == l0 + 2);
+  REQUIRE(g_launches == l0 + 5);
   REQUIRE(qsa_pool_keys(u, 128, INT64_MAX, u, 64, 1e4f, 1e-6f, 0, 16, (uint16_t*)F, nullptr) == QSA_ERR_CAPACITY);
   REQUIRE(qsa_select_mask((float*)F, INT64_MAX, INT64_MAX, (int32_t*)F, INT64_MAX, 64, 64, (uint8_t*)F,
                           (int32_t*)F, nullptr) == QSA_ERR_CAPACITY);
@@ -250,7 +292,7 @@ int main() {
                              (int32_t*)F, (int32_t*)F, nullptr) == QSA_ERR_BUDGET);
   REQUIRE(qsa_select_workspace_bytes(INT64_MAX, 262144) == 0);
   REQUIRE(qsa_score_select_workspace_bytes(INT64_MAX, 64, 4) == QSA_ERR_CAPACITY);
-  REQUIRE(g_launches == l0 + 2);
+  REQUIRE(g_launches == l0 + 5);
 
   // the sweep: every entry point, random combinations of extreme extents,
   // bad and good parameters and NULL / fake pointers
@@ -258,7 +300,7 @@ int main() {
   long counted = 0;
   for (int it = 0; it < kIters; ++it) {
     int64_t rc = 0;
-    switch (it % 18) {
+    switch (it % 20) {
       case 0:
         rc = qsa_pool_keys(P<uint16_t>(), any_int(128), any_int(4096), P<uint16_t>(), any_i32(64), any_float(1e4f),
                            any_float(1e-6f), any_int(0), any_int(1024), P<uint16_t>(), nullptr);
@@ -339,8 +381,18 @@ int main() {
         rc = qsa_select_mask_noalloc(P<float>(), any_int(65536), any_int(16 * 65536), P<int32_t>(), any_int(16),
                                      any_int(262144), any_int(2048), P<uint8_t>(), P<int32_t>(), nullptr);
         break;
+      case 18:
+        rc = qsa_pool_prep(P<uint16_t>(), any_int(128), any_int(65536), P<uint16_t>(), any_int(0), any_int(16384),
+                           P<uint16_t>(), P<uint16_t>(), any_int(512), P<int32_t>(), any_int(64), P<uint16_t>(),
+                           P<uint16_t>(), any_i32(64), any_float(1e4f), any_float(1e-6f), P<int32_t>(), nullptr);
+        break;
+      case 19:
+        rc = qsa_pool_prep_dev(P<uint16_t>(), any_int(128), any_int(65792), P<uint16_t>(), any_int(4), P<uint16_t>(),
+                               P<uint16_t>(), any_int(512), P<int32_t>(), any_int(4), P<uint16_t>(), P<uint16_t>(),
+                               any_i32(64), any_float(1e4f), any_float(1e-6f), P<int32_t>(), P<int32_t>(), nullptr);
+        break;
     }
-    const int k = it % 18;
+    const int k = it % 20;
     const bool size_query = k == 6 || k == 8 || k == 16;
     REQUIRE(size_query ? rc >= -7 : documented(rc));
     ++counted;

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.qsa_abi_version() == L.ABI_VERSION == 9
+    assert lib.qsa_abi_version() == L.ABI_VERSION == 10
     for code in range(-7, 1):
         assert lib.qsa_strerror(code)
     assert b"unknown" in lib.qsa_strerror(-99)
