@@ -30,6 +30,7 @@
 // largest visible block count of its rows (causal prefill rows are ragged).
 #include <utility>
 
+#include "prep_body.h"
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -959,6 +960,153 @@ hipError_t launch_score_ring(const ScoreArgs& s, hipStream_t stream) {
   return launch_score_ring_geom<4, false>(a, 1024, stream);
 }
 
+// ---- few decode rows: a streaming scorer ----------------------------------
+//
+// pegainfer pull request 1160 ("score QSA token-indexer blocks in native
+// CUDA"), summary: with one row the 4 heads are a sliver of a matrix tile's
+// M side, and the row's scoring is bound by the stream of pooled keys itself
+// (256 B per block, read once).  Each block is owned by 16 lanes of a wave,
+// 8 channels each.  A lane keeps its 8 channels of every head of the R
+// prepared query rows as packed bf16 pairs, forms each head dot product with
+// bf16 pair dots accumulated in f32, and the 16 lanes reduce it with DPP;
+// lane r stores row r's score (R = 1 is the one launched).  Keys are 16-byte streaming loads,
+// kStreamU per lane in flight; no LDS ring.  Without prepared queries the
+// workgroup first prepares the batch's rows into LDS (prep_body.h), so both
+// entry points run the same loop and give the same scores bit for bit.
+constexpr int kStreamU = 4;                   // blocks per 16-lane group per step
+constexpr int kStreamBlocks = 16 * kStreamU;  // blocks per workgroup step
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// Sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1).
+__device__ __forceinline__ float row16_sum_f32(float v) {
+#define QSA_ROR_STEP_F(CTRL) \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  QSA_ROR_STEP_F(0x128)
+  QSA_ROR_STEP_F(0x124)
+  QSA_ROR_STEP_F(0x122)
+  QSA_ROR_STEP_F(0x121)
+#undef QSA_ROR_STEP_F
+  return v;
+}
+
+template <int R, bool PREP>
+__global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const ScoreArgs a) {
+  static_assert(R >= 1 && R <= kPrepRows, "one prep group holds the batch");
+  static_assert(kScoreThreads == kPrepThreads, "the prep body runs on the whole workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t qs[PREP ? 8 : kPrepRows * kHeads * kHeadDim];
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4;  // block slot of this lane's 16-lane group
+  const int g = tid & 15;    // channels 8g .. 8g + 7
+  if constexpr (!PREP) {
+    PrepArgs pa{};
+    pa.q = a.q;
+    pa.q_stride = a.q_stride;
+    pa.pos = a.pos;
+    pa.rows = a.rows;
+    pa.w = a.w;
+    pa.tokens = a.tokens;
+    pa.dev_tokens = a.dev_tokens;
+    pa.qhat = qs;
+    pa.status = a.status;
+    pa.q_vec = a.q_vec;
+    pa.rp = a.rp;
+    prep_group(pa, 0);
+    __syncthreads();
+  }
+  const uint16_t* qsrc = PREP ? a.qhat : qs;
+
+  // The workgroup's first keys are requested before the row positions
+  // arrive (those come through scalar loads meanwhile), clamped to the
+  // pooled buffer -- or, with a device cache length, to its live blocks --
+  // and the visible counts only gate the stores.
+  const int64_t live = live_tokens(a.tokens, a.dev_tokens, a.status);
+  const int64_t nb_cap = live / kRatio;
+  typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+  u32x4_nt kv[kStreamU];
+  auto load_keys = [&](int64_t b0) {
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const int64_t b = b0 + grp + 16 * u;
+      const int64_t bc = b < nb_cap ? b : nb_cap - 1;
+      kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(a.pooled + bc * kHeadDim + 8 * g));
+    }
+  };
+  int64_t b0 = static_cast<int64_t>(blockIdx.x) * kStreamBlocks;
+  if (b0 < nb_cap) load_keys(b0);  // uniform
+
+  // this lane's query channels of every row and head (also ahead of the positions)
+  uint32_t qv[R][kHeads][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < a.rows) v = *reinterpret_cast<const uint4*>(qsrc + r * (kHeads * kHeadDim) + h * kHeadDim + 8 * g);
+      qv[r][h][0] = v.x;
+      qv[r][h][1] = v.y;
+      qv[r][h][2] = v.z;
+      qv[r][h][3] = v.w;
+    }
+  // rows and their visible block counts (uniform across the workgroup)
+  int nv[R];
+  int nmax = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    nv[r] = 0;
+    if (r < a.rows) {
+      const int p = a.pos[r];
+      if (p >= 0 && p < live)
+        nv[r] = (p + 1) / kRatio;
+      else if (blockIdx.x == 0 && tid == 0)
+        atomicOr(a.status, 1);
+    }
+    nmax = max(nmax, nv[r]);
+  }
+
+  // nmax <= nb_cap, so a workgroup that skipped its loads never enters
+  while (b0 < nmax) {
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const int64_t b = b0 + grp + 16 * u;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float d[kHeads];
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) {
+          float acc = dot2_bf16(qv[r][h][0], kv[u][0], 0.0f);
+          acc = dot2_bf16(qv[r][h][1], kv[u][1], acc);
+          acc = dot2_bf16(qv[r][h][2], kv[u][2], acc);
+          acc = dot2_bf16(qv[r][h][3], kv[u][3], acc);
+          d[h] = row16_sum_f32(acc);
+        }
+        if (g == r && b < nv[r]) {
+          float sc = score_fast(d[0], d[1], d[2], d[3]);
+          if (!(__float_as_uint(sc) < 0x7F800000u)) sc = score_exact(d[0], d[1], d[2], d[3]);
+          a.scores[r * a.score_cols + b] = sc;
+        }
+      }
+    }
+    b0 += static_cast<int64_t>(gridDim.x) * kStreamBlocks;
+    if (b0 < nmax) load_keys(b0);
+  }
+}
+
+template <bool PREP>
+hipError_t launch_score_stream(const ScoreArgs& a, hipStream_t stream) {
+  const int64_t nb = a.tokens / kRatio;
+  int64_t grid = (nb + kStreamBlocks - 1) / kStreamBlocks;
+  grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);  // one workgroup still flags bad positions
+  const dim3 g(static_cast<unsigned>(grid)), b(kScoreThreads);
+  score_stream_kernel<1, PREP><<<g, b, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int WM, int MS, int D, bool PREP>
 hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
   using G = ScoreGeom<WM, MS, D, PREP>;
@@ -994,17 +1142,24 @@ hipError_t launch_score_geom(const ScoreArgs& base, hipStream_t stream) {
 
 template <bool PREP>
 hipError_t launch_score_rows(const ScoreArgs& a, hipStream_t stream) {
-  // Prepared queries: 32 rows per wave when there are enough rows, so each
-  // B fragment feeds four MFMAs.  The one-call path keeps 8 rows per wave,
-  // which bounds its query-prep LDS.
+  // The one-call path keeps 8 rows per wave, which bounds its query-prep LDS.
   // Prepared queries in batches of 128 rows and more: the ring scorer, when
   // its store resource fits.  (Its 1- and 2-wave-row layouts measured slower
   // than the kernels below on decode batches: 32 A-fragment loads and a
   // 96 KiB ring per workgroup outweigh the shared key tiles there.)
+  // One row: the streaming scorer (64k: 3.0 us per launch against 4.2 for
+  // the padded-M matrix kernel).  From two rows its per-row lane reductions
+  // make it VALU-bound (two rows over 256k: 7.3 us against 5.0), and the
+  // matrix kernels below take over.
+  if (a.rows == 1) return launch_score_stream<PREP>(a, stream);
   if constexpr (PREP)
     if (a.rows >= 128 && ring_fits(a, 128)) return launch_score_ring(a, stream);
+  // 64..127 prepared rows: one 64-row group, each wave 16 rows (two
+  // subtiles) of a 32-block tile, so no two waves load the same A fragments
+  // (64 rows over 64k: 7.9 -> 6.0 us against 32 rows per wave and 64-block
+  // tiles, whose waves load every fragment twice).
   if constexpr (PREP)
-    if (a.rows >= 64) return launch_score_geom<2, 4, 4, PREP>(a, stream);
+    if (a.rows >= 64) return launch_score_geom<4, 2, 4, PREP>(a, stream);
   if (a.rows >= 32) return launch_score_geom<4, 1, 4, PREP>(a, stream);
   if (a.rows > 8) return launch_score_geom<2, 1, 4, PREP>(a, stream);
   return launch_score_geom<1, 1, 3, PREP>(a, stream);

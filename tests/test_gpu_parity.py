@@ -578,6 +578,89 @@ def test_score_prepped_equals_fused_bitwise(wid):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def few_row_positions(T, R):
+    """Ragged positions for a batch of R <= 4 rows: the cache's last token,
+    a mid-cache row, a row inside its first block and a row with a partial
+    last block."""
+    return np.array([T - 1, T // 2 + 3, 2, 4 * 1001 + 2][:R], dtype=np.int32)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+@pytest.mark.parametrize("wid", [3, 4])
+def test_score_few_rows_against_oracle(wid, R):
+    """Batches of one to four rows (one row: the streaming scorer; more: the
+    matrix kernels): both entry points within the bound of the oracle on
+    ragged rows, nothing written past a row's prefix into the spare columns,
+    and the two entry points equal bit for bit."""
+    w = workload(wid)
+    T = w["tokens"]
+    pos = few_row_positions(T, R)
+    q = w["queries"][:R]
+    cols = T // 4 + 5
+    sentinel = np.float32(-7.25)
+    note(f"score: {R} rows over workload {wid} ({T} tokens), both entry points")
+    pooled = u16_dev(oracle_pooled(wid))
+    a, s1 = gpu_scores(w, pooled, pos=pos, q=q, score_cols=cols, sentinel=sentinel)
+    b, s2 = gpu_scores_prepped(w, pooled, pos=pos, q=q, score_cols=cols, sentinel=sentinel)
+    assert s1 == s2 == 0
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    qhat = O.prep_queries(q, pos, w["q_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    want = O.score_rows(qhat, pos, oracle_pooled(wid), T)
+    worst = 0.0
+    for r, sc in enumerate(want):
+        n = len(sc)
+        assert n == (pos[r] + 1) // 4
+        assert np.all(a[r, n:] == sentinel), "wrote past the visible prefix"
+        if n:
+            worst = max(worst, float(np.abs(a[r, :n].astype(np.float64) - sc).max()))
+    note(f"  max |gpu - oracle| = {worst:.3e}")
+    assert worst <= SCORE_ATOL
+
+
+@pytest.mark.parametrize("path", ["fused", "prepped"])
+def test_score_few_rows_nan_key_and_bad_positions(path):
+    """The streaming scorer's edges: a NaN key poisons exactly its block,
+    rows with out-of-range positions are flagged and left untouched."""
+    w = workload(1)
+    pooled = oracle_pooled(1).copy()
+    pooled[50] = 0x7FC0
+    pos = np.array([203, -3, 512, 60], dtype=np.int32)
+    q = w["queries"][: len(pos)]
+    note(f"score ({path}): 4 rows, NaN key, bad positions")
+    got, st = SCORERS[path](w, u16_dev(pooled), pos=pos, q=q)
+    assert st == O.STATUS_BAD_POSITION
+    assert np.all(got[1] == np.float32(-7.25)) and np.all(got[2] == np.float32(-7.25))
+    assert np.isnan(got[0, 50]) and np.all(np.isfinite(np.delete(got[0, :51], 50)))
+    assert np.all(np.isfinite(got[3, :15])) and np.all(got[3, 15:] == np.float32(-7.25))
+    qhat = O.prep_queries(q[[0, 3]], pos[[0, 3]], w["q_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    want = O.score_rows(qhat, pos[[0, 3]], pooled, 512)
+    ok = ~np.isnan(want[0])
+    assert np.all(np.abs(got[0, :51][ok].astype(np.float64) - want[0][ok]) <= SCORE_ATOL)
+    assert np.all(np.abs(got[3, :15].astype(np.float64) - want[1]) <= SCORE_ATOL)
+
+
+@pytest.mark.parametrize("path", ["fused", "prepped"])
+def test_score_one_row_nan_key_and_bad_position(path):
+    """The streaming scorer (one row): a NaN key poisons exactly its block;
+    a row at a position past the cache is flagged and left untouched."""
+    w = workload(1)
+    pooled = oracle_pooled(1).copy()
+    pooled[50] = 0x7FC0
+    note(f"score ({path}): one row, NaN key; one row, bad position")
+    got, st = SCORERS[path](w, u16_dev(pooled), pos=np.array([203], np.int32), q=w["queries"][:1])
+    assert st == 0
+    assert np.isnan(got[0, 50]) and np.all(np.isfinite(np.delete(got[0, :51], 50)))
+    assert np.all(got[0, 51:] == np.float32(-7.25))
+    qhat = O.prep_queries(w["queries"][:1], np.array([203], np.int32), w["q_norm_w"], w["rotary_dim"],
+                          w["theta"], w["eps"])
+    want = O.score_rows(qhat, np.array([203], np.int32), pooled, 512)[0]
+    ok = ~np.isnan(want)
+    assert np.all(np.abs(got[0, :51][ok].astype(np.float64) - want[ok]) <= SCORE_ATOL)
+    got, st = SCORERS[path](w, u16_dev(pooled), pos=np.array([512], np.int32), q=w["queries"][:1])
+    assert st == O.STATUS_BAD_POSITION
+    assert np.all(got == np.float32(-7.25))
+
+
 def test_score_duplicate_blocks_tie_exactly():
     w = workload(1)
     pooled = u16_dev(oracle_pooled(1))
@@ -746,13 +829,14 @@ def _compare_huge(got, want, pos):
         assert np.all(err <= 5e-3 + 2.0 ** -16 * np.abs(s[fin])), (r, float(err.max()))
 
 
-@pytest.mark.parametrize("R", [8, 70, 130])
+@pytest.mark.parametrize("R", [1, 4, 8, 70, 130])
 def test_score_head_dots_past_half_range_and_minus_inf(R):
     """relu is a comparison: a head dot of -Inf contributes 0, and head dots
     above 2^127 (whose doubled relu terms would overflow) keep their finite
     score, as in the oracle; two such heads overflow the f32 head sum to
-    +Inf there too.  Prepared queries through the decode kernels (8 and 70
-    rows) and the ring scorer (130 rows)."""
+    +Inf there too.  Prepared queries through the streaming scorer (1 and 4
+    rows), the decode kernels (8 and 70 rows) and the ring scorer (130
+    rows)."""
     T, keys, qs, pos = _huge_dot_inputs(R)
     import warnings
     with warnings.catch_warnings():
