@@ -88,6 +88,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[3 * 256];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint64_t cand[kPrefilter ? kCandCap : 1];
+  __shared__ uint32_t ccount;  // candidates compacted (one LDS atomic per wave)
   __shared__ uint32_t kbits[kWords];
 
   const int tid = threadIdx.x;
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
     for (int j = 0; j < KPT; ++j) key[j] = 0u;
   }
   if (tid < 256) hist[tid] = 0u;  // first radix buffer; the next barrier publishes it
+  if (tid == 0) ccount = 0u;
   if constexpr (IDX)
     for (int i = tid; i < kWords; i += NT) kbits[i] = 0u;
   if (__syncthreads_or(bad)) {
@@ -222,30 +224,32 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
         L = red[w] < L ? red[w] : L;
         kmax = red[NW + w] > kmax ? red[NW + w] : kmax;
       }
-      // count and compact the candidates key >= L
+      // count and compact the candidates key >= L: each wave takes its slot
+      // range with one LDS atomic (candidate order does not matter to the
+      // search); writes past the capacity are dropped, and such a total
+      // sends the row to the exact search over all keys below
       uint32_t mine = 0;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) mine += key[j] >= L ? 1u : 0u;
       const uint32_t incl = wave_incl_sum(mine);
-      __syncthreads();  // every wave has read red[]
-      if (lane == 63) red[wave] = incl;
-      __syncthreads();
-      uint32_t base = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        base += w < wave ? red[w] : 0u;
-        total += red[w];
-      }
-      if (total <= static_cast<uint32_t>(kCandCap)) {
-        uint32_t at = base + incl - mine;
+      uint32_t wbase = 0;
+      if (lane == 63) wbase = atomicAdd(&ccount, incl);
+      uint32_t at = read_lane(wbase, 63) + incl - mine;
+      {
         const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
           const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
           const uint32_t kk = opaque(key[j]);
-          if (kk >= L) cand[at++] = composite(kk, b);
+          if (kk >= L) {
+            if (at < static_cast<uint32_t>(kCandCap)) cand[at] = composite(kk, b);
+            ++at;
+          }
         }
-        __syncthreads();
+      }
+      __syncthreads();  // every wave has read red[], counted and written
+      const uint32_t total = ccount;
+      if (total <= static_cast<uint32_t>(kCandCap)) {
         const int c = static_cast<int>(total);
         cstar = radix_threshold<NT>(
             [&](auto f) {

@@ -61,6 +61,7 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[3 * 256];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint64_t lcand[kCandCap];
+  __shared__ uint32_t ccount;  // candidates compacted (one LDS atomic per wave)
   __shared__ uint32_t wsum[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
     }
   }
   if (tid < 256) hist[tid] = 0u;
+  if (tid == 0) ccount = 0u;
   if (__syncthreads_or(bad)) {
     if (tid == 0) {
       atomicOr(a.status, QSA_STATUS_NONFINITE_SCORE);
@@ -170,29 +172,31 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
         L = red[w] < L ? red[w] : L;
         kmax = red[NW + w] > kmax ? red[NW + w] : kmax;
       }
+      // compaction: one LDS atomic per wave for its slot range (order does
+      // not matter to the search); writes past the capacity are dropped and
+      // such a total takes the exact search over all keys below
       uint32_t mine = 0;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) mine += key[j] >= L ? 1u : 0u;
       const uint32_t incl = wave_incl_sum(mine);
-      __syncthreads();
-      if (lane == 63) red[wave] = incl;
-      __syncthreads();
-      uint32_t base = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        base += w < wave ? red[w] : 0u;
-        total += red[w];
-      }
-      if (total <= static_cast<uint32_t>(kCandCap)) {
-        uint32_t at = base + incl - mine;
+      uint32_t wbase = 0;
+      if (lane == 63) wbase = atomicAdd(&ccount, incl);
+      uint32_t at = read_lane(wbase, 63) + incl - mine;
+      {
         const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
           const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
           const uint32_t kk = opaque(key[j]);
-          if (kk >= L) lcand[at++] = composite(kk, b);
+          if (kk >= L) {
+            if (at < static_cast<uint32_t>(kCandCap)) lcand[at] = composite(kk, b);
+            ++at;
+          }
         }
-        __syncthreads();
+      }
+      __syncthreads();  // every wave has read red[], counted and written
+      const uint32_t total = ccount;
+      if (total <= static_cast<uint32_t>(kCandCap)) {
         const int c = static_cast<int>(total);
         cstar = radix_threshold<NT>(
             [&](auto f) {
@@ -281,6 +285,7 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[3 * 256];
   __shared__ uint32_t red[2 * NW];
   __shared__ uint64_t lcand[kCandCap];
+  __shared__ uint32_t ccount;  // candidates compacted (one LDS atomic per wave)
   __shared__ int cnts[64];
   __shared__ int offs[65];
   __shared__ int kcount[64];  // index mode: kept blocks per chunk
@@ -369,6 +374,7 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
   if (tid < 64) kcount[tid] = 0;
   if (tid < kSplitChunk / 32) keptbits[tid] = 0u;
   if (tid < 256) hist[tid] = 0u;
+  if (tid == 0) ccount = 0u;
   __syncthreads();
   if (tid == 0) {
     int acc = 0;
@@ -417,23 +423,20 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) mine += static_cast<uint32_t>(cv[j] >> 32) >= L ? 1u : 0u;
   const uint32_t incl = wave_incl_sum(mine);
-  __syncthreads();
-  if (lane == 63) red[wave] = incl;
-  __syncthreads();
-  uint32_t wbase = 0, ctotal = 0;
+  uint32_t wbase = 0;
+  if (lane == 63) wbase = atomicAdd(&ccount, incl);
+  uint32_t at = read_lane(wbase, 63) + incl - mine;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    wbase += w < wave ? red[w] : 0u;
-    ctotal += red[w];
-  }
+  for (int j = 0; j < KPT; ++j)
+    if (static_cast<uint32_t>(cv[j] >> 32) >= L) {
+      if (at < static_cast<uint32_t>(kCandCap)) lcand[at] = cv[j];
+      ++at;
+    }
+  __syncthreads();  // every wave has read red[], counted and written
+  const uint32_t ctotal = ccount;
   uint64_t cstar;
   uint32_t lowkey;
   if (ctotal <= static_cast<uint32_t>(kCandCap)) {
-    uint32_t at = wbase + incl - mine;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (static_cast<uint32_t>(cv[j] >> 32) >= L) lcand[at++] = cv[j];
-    __syncthreads();
     const int c = static_cast<int>(ctotal);
     cstar = radix_threshold<NT>(
         [&](auto f) {
