@@ -101,31 +101,6 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   const int64_t p = a.pos[row];
   const int64_t live = live_tokens(T, a.dev_tokens, a.status);
 
-  // The row's scores are requested before its position arrives: the loads
-  // cover the buffer's first T / 4 columns (clamped there, so they stay in
-  // the row) and the keys below keep only the visible prefix.
-  const float* srow = a.scores + row * a.score_cols;
-  const int ncap = static_cast<int>(T / kRatio);  // at most KPT * NT by the dispatch
-  float4 v[VEC ? KPT / 4 : 1];
-  float sv[VEC ? 1 : KPT];
-  if (ncap > 0) {  // uniform
-    if constexpr (VEC) {
-      const float4* s4 = reinterpret_cast<const float4*>(srow);
-      const int qcap = (ncap - 1) >> 2;
-#pragma unroll
-      for (int g = 0; g < KPT / 4; ++g) {
-        const int q = tid + g * NT;
-        v[g] = load_stream(s4 + (q < qcap ? q : qcap));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int b = tid + j * NT;
-        sv[j] = srow[b < ncap ? b : ncap - 1];
-      }
-    }
-  }
-
   const int cap = 4 * a.keep_max + 3;  // index mode: entries per row
   int32_t* irow = IDX ? a.idx + row * a.idx_stride : nullptr;
   // index mode, rows without a selection: entries i <= last are i, the rest -1
@@ -149,11 +124,22 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   auto blk = [&](int j) { return VEC ? 4 * (tid + (j >> 2) * NT) + (j & 3) : tid + j * NT; };
 
   // ---- the visible prefix as order-keys (0 = absent; a finite score's key
-  // is at least 0x00800000).
+  // is at least 0x00800000).  The loads wait for the position: clamped to
+  // the row's own prefix they stay within the lines the scorer wrote (a
+  // causal prefill row's prefix is shorter than the buffer's width).
+  const float* srow = a.scores + row * a.score_cols;
   uint32_t key[KPT];
   int bad = 0;
   if (n > 0) {
     if constexpr (VEC) {
+      const float4* s4 = reinterpret_cast<const float4*>(srow);
+      const int qlast = (n - 1) >> 2;
+      float4 v[KPT / 4];
+#pragma unroll
+      for (int g = 0; g < KPT / 4; ++g) {
+        const int q = tid + g * NT;
+        v[g] = load_stream(s4 + (q < qlast ? q : qlast));
+      }
 #pragma unroll
       for (int g = 0; g < KPT / 4; ++g) {
         const float e[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
@@ -165,6 +151,12 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
         }
       }
     } else {
+      float sv[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int b = blk(j);
+        sv[j] = srow[b < n ? b : n - 1];
+      }
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const bool vis = blk(j) < n;
