@@ -216,6 +216,30 @@ def back_to_back_us(d: Device, torch, reps: int = 20):
     return out
 
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def launch_floor_us(torch, reps: int = 50):
+    """Microseconds per launch of a one-element fill (torch's own kernel)
+    launched back to back behind a busy GPU: the per-kernel floor that every
+    launch in a dependent chain pays, whatever it computes."""
+    x = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        x.fill_(1.0)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    prime(torch)
+    a.record(stream)
+    for _ in range(reps):
+        x.fill_(1.0)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1e3 / reps, 3)
+
+
 def flush_caches(flush):
     """Read a 512 MiB buffer: evicts L2 and the MALL without leaving dirty
     lines whose write-back would land in the next measurement, and keeps the
@@ -299,8 +323,8 @@ STAGE_KERNELS = {"pool": "pool_kernel", "prep": "prep_kernel", "pool_prep": "poo
 
 def kernel_base(name: str) -> str:
     """Unqualified kernel name without template arguments or parameters."""
-    n = name.replace("void ", "").split("(")[0].split("<")[0]
-    return n.split("::")[-1]
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return n.split("(")[0].split("<")[0].split("::")[-1]
 
 
 def stage_of(name: str, stage: str) -> bool:
@@ -635,7 +659,7 @@ def side_figures(torch, qsa, synth):
     decode workloads and the one-row 64k/256k shapes: per-kernel event means over 20 launches after 5 warm-ups
     (each launch between its own event pair), per-kernel back-to-back launch
     times, and the cold-cache step with its aggregate HBM fraction."""
-    out = {}
+    out = {"launch_floor_us": launch_floor_us(torch)}
     for key, w in (("prefill_4k", synth.make_workload(2)),
                    ("decode_64k_x64", synth.make_workload(3)),
                    ("decode_256k_x16", synth.make_workload(4)),
@@ -663,6 +687,7 @@ def side_figures(torch, qsa, synth):
                     "kernels": rep}
         if key != "prefill_4k":  # decode consumers of the selection
             out[key].update(decode_next(d, torch, qsa))
+        progress(f"side workload {key} measured")
         del d
         torch.cuda.empty_cache()
     return out
@@ -688,6 +713,7 @@ def main():
     w = synth.make_workload(args.workload)
     d = Device(w, torch, qsa)
     wall, per, dom = time_steps(d, args.steps, args.warmup, torch)
+    progress(f"{args.steps} timed steps done")
     st = qsa.check_status(d.status)
     if st != 0:
         raise RuntimeError(f"device status {st} on a clean workload")
@@ -714,6 +740,7 @@ def main():
     side = {} if args.no_side else side_figures(torch, qsa, synth)
     fused = None if args.no_side else fused_prefill(d, torch, qsa)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    progress("cpu baseline done")
 
     line = {
         "metric": "scored (row,block) pairs/s + select+mask us/row at 64k and 256k ctx",
