@@ -240,3 +240,44 @@ def test_device_count_past_the_ceiling_is_clamped_and_flagged():
     assert int(b["st"].item()) == qsa.STATUS_BAD_GEOMETRY
     ref = s.reference(CEIL)
     assert torch.equal(b["idx"], ref["idx"]) and torch.equal(b["ko"], ref["ko"])
+
+
+def test_one_row_device_count_scorer_against_the_oracle():
+    """The one-row streaming scorer with the live cache length on the device
+    (its key loads are clamped to the live blocks, not the ceiling): one row
+    at T - 1 for cache lengths well below the ceiling, with no complete
+    block, and past the ceiling (clamped and flagged); scores within the
+    bound of the oracle, nothing written past the prefix, and equal bit for
+    bit to the host-count call at the same length."""
+    s = Setup()
+    oref = OracleRef(s)
+    w = s.w
+    rd, th, eps = s.rope()
+    pooled = torch.from_numpy(oref.pooled.view(np.int16)).to(DEV)
+    q1 = s.q[:1]
+    cols = CEIL // 4
+    for T in (CEIL, CEIL - 200, 40001, 7, 3):
+        note(f"one-row device-count scorer: T={T} of {CEIL}")
+        pos = torch.full((1,), T - 1, dtype=torch.int32, device=DEV)
+        dt = torch.full((1,), T, dtype=torch.int32, device=DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        qhat = torch.zeros((1, 4, 128), dtype=torch.int16, device=DEV)
+        qsa.qsa_prep_queries(q1, pos, s.wq, rd, th, eps, T, qhat, st)
+        sc = torch.full((cols,), -7.25, dtype=torch.float32, device=DEV)
+        qsa.qsa_score_prepped_dev(qhat, pos, pooled, dt, CEIL, sc, cols, st)
+        ref = torch.full((cols,), -7.25, dtype=torch.float32, device=DEV)
+        qsa.qsa_score_prepped(qhat, pos, pooled, T, ref, cols, st)
+        assert qsa.check_status(st) == 0
+        n = T // 4
+        got = sc.cpu().numpy()
+        assert np.all(got[n:] == np.float32(-7.25)), f"wrote past the prefix at T={T}"
+        assert torch.equal(sc.view(torch.int32), ref.view(torch.int32)), f"device count vs host count at T={T}"
+        qh = O.prep_queries(w["queries"][:1], np.array([T - 1], np.int32), w["q_norm_w"], rd, th, eps)
+        want = O.score_rows(qh, np.array([T - 1], np.int32), oref.pooled[:n], T)[0]
+        if n:
+            assert np.max(np.abs(got[:n].astype(np.float64) - want)) <= 5e-3, f"scores past the bound at T={T}"
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sc = torch.full((cols,), -7.25, dtype=torch.float32, device=DEV)
+    qsa.qsa_score_prepped_dev(qhat, torch.full((1,), CEIL - 1, dtype=torch.int32, device=DEV), pooled,
+                              torch.full((1,), CEIL + 9, dtype=torch.int32, device=DEV), CEIL, sc, cols, st)
+    assert qsa.check_status(st) == qsa.STATUS_BAD_GEOMETRY
