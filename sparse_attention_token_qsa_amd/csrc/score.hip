@@ -960,19 +960,19 @@ hipError_t launch_score_ring(const ScoreArgs& s, hipStream_t stream) {
   return launch_score_ring_geom<4, false>(a, 1024, stream);
 }
 
-// ---- few decode rows: a streaming scorer ----------------------------------
+// ---- one decode row: a streaming scorer -----------------------------------
 //
 // pegainfer pull request 1160 ("score QSA token-indexer blocks in native
 // CUDA"), summary: with one row the 4 heads are a sliver of a matrix tile's
 // M side, and the row's scoring is bound by the stream of pooled keys itself
 // (256 B per block, read once).  Each block is owned by 16 lanes of a wave,
-// 8 channels each.  A lane keeps its 8 channels of every head of the R
-// prepared query rows as packed bf16 pairs, forms each head dot product with
-// bf16 pair dots accumulated in f32, and the 16 lanes reduce it with DPP;
-// lane r stores row r's score (R = 1 is the one launched).  Keys are 16-byte streaming loads,
+// 8 channels each.  A lane keeps its 8 channels of the 4 prepared heads as
+// packed bf16 pairs, forms each head dot product with bf16 pair dots
+// accumulated in f32, and the 16 lanes reduce it with DPP; lane 0 of the
+// group stores the block's score.  Keys are 16-byte streaming loads,
 // kStreamU per lane in flight; no LDS ring.  Without prepared queries the
-// workgroup first prepares the batch's rows into LDS (prep_body.h), so both
-// entry points run the same loop and give the same scores bit for bit.
+// workgroup first prepares the row into LDS (prep_body.h), so both entry
+// points run the same loop and give the same scores bit for bit.
 constexpr int kStreamU = 4;                   // blocks per 16-lane group per step
 constexpr int kStreamBlocks = 16 * kStreamU;  // blocks per workgroup step
 
@@ -995,9 +995,8 @@ __device__ __forceinline__ float row16_sum_f32(float v) {
   return v;
 }
 
-template <int R, bool PREP>
+template <bool PREP>
 __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const ScoreArgs a) {
-  static_assert(R >= 1 && R <= kPrepRows, "one prep group holds the batch");
   static_assert(kScoreThreads == kPrepThreads, "the prep body runs on the whole workgroup");
   __shared__ __attribute__((aligned(16))) uint16_t qs[PREP ? 8 : kPrepRows * kHeads * kHeadDim];
   const int tid = threadIdx.x;
@@ -1008,7 +1007,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
     pa.q = a.q;
     pa.q_stride = a.q_stride;
     pa.pos = a.pos;
-    pa.rows = a.rows;
+    pa.rows = 1;
     pa.w = a.w;
     pa.tokens = a.tokens;
     pa.dev_tokens = a.dev_tokens;
@@ -1021,10 +1020,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
   }
   const uint16_t* qsrc = PREP ? a.qhat : qs;
 
-  // The workgroup's first keys are requested before the row positions
-  // arrive (those come through scalar loads meanwhile), clamped to the
-  // pooled buffer -- or, with a device cache length, to its live blocks --
-  // and the visible counts only gate the stores.
+  // The workgroup's first keys are requested before the row's position
+  // arrives, clamped to the pooled buffer -- or, with a device cache length,
+  // to its live blocks -- and the visible count only gates the stores.
   const int64_t live = live_tokens(a.tokens, a.dev_tokens, a.status);
   const int64_t nb_cap = live / kRatio;
   typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
@@ -1040,60 +1038,46 @@ __global__ __launch_bounds__(kScoreThreads) void score_stream_kernel(const Score
   int64_t b0 = static_cast<int64_t>(blockIdx.x) * kStreamBlocks;
   if (b0 < nb_cap) load_keys(b0);  // uniform
 
-  // this lane's query channels of every row and head (also ahead of the positions)
-  uint32_t qv[R][kHeads][4];
+  // this lane's channels of the 4 heads (also requested ahead of the position)
+  uint32_t qv[kHeads][4];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int h = 0; h < kHeads; ++h) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < a.rows) v = *reinterpret_cast<const uint4*>(qsrc + r * (kHeads * kHeadDim) + h * kHeadDim + 8 * g);
-      qv[r][h][0] = v.x;
-      qv[r][h][1] = v.y;
-      qv[r][h][2] = v.z;
-      qv[r][h][3] = v.w;
-    }
-  // rows and their visible block counts (uniform across the workgroup)
-  int nv[R];
-  int nmax = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    nv[r] = 0;
-    if (r < a.rows) {
-      const int p = a.pos[r];
-      if (p >= 0 && p < live)
-        nv[r] = (p + 1) / kRatio;
-      else if (blockIdx.x == 0 && tid == 0)
-        atomicOr(a.status, 1);
-    }
-    nmax = max(nmax, nv[r]);
+  for (int h = 0; h < kHeads; ++h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(qsrc + h * kHeadDim + 8 * g);
+    qv[h][0] = v.x;
+    qv[h][1] = v.y;
+    qv[h][2] = v.z;
+    qv[h][3] = v.w;
   }
+  // the row's visible block count (uniform across the workgroup)
+  const int p = a.pos[0];
+  int n = 0;
+  if (p >= 0 && p < live)
+    n = (p + 1) / kRatio;
+  else if (blockIdx.x == 0 && tid == 0)
+    atomicOr(a.status, 1);
 
-  // nmax <= nb_cap, so a workgroup that skipped its loads never enters
-  while (b0 < nmax) {
+  // n <= nb_cap, so a workgroup that skipped its loads never enters
+  while (b0 < n) {
 #pragma unroll
     for (int u = 0; u < kStreamU; ++u) {
       const int64_t b = b0 + grp + 16 * u;
+      float d[kHeads];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float d[kHeads];
-#pragma unroll
-        for (int h = 0; h < kHeads; ++h) {
-          float acc = dot2_bf16(qv[r][h][0], kv[u][0], 0.0f);
-          acc = dot2_bf16(qv[r][h][1], kv[u][1], acc);
-          acc = dot2_bf16(qv[r][h][2], kv[u][2], acc);
-          acc = dot2_bf16(qv[r][h][3], kv[u][3], acc);
-          d[h] = row16_sum_f32(acc);
-        }
-        if (g == r && b < nv[r]) {
-          float sc = score_fast(d[0], d[1], d[2], d[3]);
-          if (!(__float_as_uint(sc) < 0x7F800000u)) sc = score_exact(d[0], d[1], d[2], d[3]);
-          a.scores[r * a.score_cols + b] = sc;
-        }
+      for (int h = 0; h < kHeads; ++h) {
+        float acc = dot2_bf16(qv[h][0], kv[u][0], 0.0f);
+        acc = dot2_bf16(qv[h][1], kv[u][1], acc);
+        acc = dot2_bf16(qv[h][2], kv[u][2], acc);
+        acc = dot2_bf16(qv[h][3], kv[u][3], acc);
+        d[h] = row16_sum_f32(acc);
+      }
+      if (g == 0 && b < n) {
+        float sc = score_fast(d[0], d[1], d[2], d[3]);
+        if (!(__float_as_uint(sc) < 0x7F800000u)) sc = score_exact(d[0], d[1], d[2], d[3]);
+        a.scores[b] = sc;
       }
     }
     b0 += static_cast<int64_t>(gridDim.x) * kStreamBlocks;
-    if (b0 < nmax) load_keys(b0);
+    if (b0 < n) load_keys(b0);
   }
 }
 
@@ -1103,7 +1087,7 @@ hipError_t launch_score_stream(const ScoreArgs& a, hipStream_t stream) {
   int64_t grid = (nb + kStreamBlocks - 1) / kStreamBlocks;
   grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);  // one workgroup still flags bad positions
   const dim3 g(static_cast<unsigned>(grid)), b(kScoreThreads);
-  score_stream_kernel<1, PREP><<<g, b, 0, stream>>>(a);
+  score_stream_kernel<PREP><<<g, b, 0, stream>>>(a);
   return hipGetLastError();
 }
 
