@@ -4,7 +4,7 @@
 // pegainfer pull request 1160 ("score QSA token-indexer blocks in native
 // CUDA"), summary: the query heads are normed and roped at the row position
 // before the dot products; the norm and rotary conventions are those of the
-// pooled keys (pool.hip), with bf16 rounding after the norm and after every
+// pooled keys (pool_body.h), with bf16 rounding after the norm and after every
 // rotary product and sum.
 //
 // Workgroup: 256 threads = 4 rows = 16 head vectors; 16 lanes per head
