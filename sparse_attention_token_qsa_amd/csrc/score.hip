@@ -549,6 +549,43 @@ __device__ __forceinline__ int lds_read_word(uint32_t addr) {
   return v;
 }
 
+// In-register transpose of one emit phase.  On entry slot s (0..7) of lane
+// (r, h) = lane % 32, lane / 32 holds phase row 2 s + h at tile block r.
+// Three exchanges trade the slot index bits s2, s1, s0 for the lane bits 4,
+// 1, 0: a permlane16 swap (lane bit 4), then quad permutations taken by the
+// lanes whose bit is set (lane bits 1 and 0).  On exit lane l holds, in slot
+// j, phase row 8 l[4] + 4 l[1] + 2 l[0] + l[5] at tile block
+// 16 j[2] + 4 ((l >> 2) & 3) + (j & 3).
+__device__ __forceinline__ void emit_transpose(uint32_t (&v)[8], int lane) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v[s], v[s + 4], false, false);
+    v[s] = p[0];
+    v[s + 4] = p[1];
+  }
+  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = (k & 1) + 4 * (k >> 1);  // 0, 1, 4, 5: partners s + 2
+    const uint32_t pa = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v[s]), 0x4E, 0xF, 0xF, false));
+    const uint32_t pb = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v[s + 2]), 0x4E, 0xF, 0xF, false));
+    const uint32_t na = b1 ? pb : v[s];
+    const uint32_t nb = b1 ? v[s + 2] : pa;
+    v[s] = na;
+    v[s + 2] = nb;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = 2 * k;  // partners s + 1
+    const uint32_t pa = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v[s]), 0xB1, 0xF, 0xF, false));
+    const uint32_t pb = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v[s + 1]), 0xB1, 0xF, 0xF, false));
+    const uint32_t na = b0 ? pb : v[s];
+    const uint32_t nb = b0 ? v[s + 1] : pa;
+    v[s] = na;
+    v[s + 1] = nb;
+  }
+}
+
 // EMIT: instead of storing the scores, the kernel keeps the blocks whose
 // score, read as an unsigned integer, is at least the row's threshold
 // thr[row] (score bits).  Scores are +-0 or positive or NaN: for finite
@@ -556,13 +593,13 @@ __device__ __forceinline__ int lds_read_word(uint32_t addr) {
 // reads as large and is kept, which only adds a candidate), and NaN / +Inf
 // bits lie above every threshold up to +Inf: non-finite scores are always
 // kept, for the selector to refuse.  Each epilogue phase (16 rows x 32
-// blocks of a wave) goes through a small LDS tile so that lane l owns row
-// l / 4 of the phase and blocks 8 (l % 4) .. + 7 of the tile: its threshold
+// blocks of a wave) is transposed in registers (emit_transpose) so that each
+// lane owns one row of the phase and eight blocks of the tile: its threshold
 // and its running count stay in the lane, and a kept block is one compare and
 // one store, with no cross-lane work.  Kept blocks go to the region of (row,
-// split, l % 4), cap entries of (score bits, block); the counts, which may
-// exceed cap (the excess overwrote the region's last entry), finally go to
-// cnt[row][split][l % 4].
+// split, block group), cap entries of (score bits, block); the counts, which
+// may exceed cap (the excess overwrote the region's last entry), finally go
+// to cnt[row][split][block group].
 template <int WM, bool EMIT>
 __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   using G = RingGeom<WM>;
@@ -571,11 +608,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[D * STAGE];
   __shared__ int nvis[RG];
   __shared__ int sh_nmax, sh_nmin;
-  // EMIT: per-row thresholds, and one 16 x 32 sum tile per wave (row pitch
-  // 36 words keeps 16-byte reads aligned)
-  constexpr int kEPitch = 36;
-  __shared__ uint32_t sthr[EMIT ? RG : 1];
-  __shared__ __attribute__((aligned(16))) uint32_t etile[EMIT ? 4 * 16 * kEPitch : 1];
+  __shared__ uint32_t sthr[EMIT ? RG : 1];  // EMIT: per-row thresholds
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = wave % WM;   // 32-row slice of the group
@@ -594,10 +627,13 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   const int blk_begin = split * TILE;
   const int stride = a.splits * TILE;
 
-  // EMIT: lane l's rows are 32 m + l / 4 (phase of acc[0..1]) and 32 m + 16 +
-  // l / 4 (acc[2..3]); its blocks of a tile are 8 (l % 4) .. + 7
-  const int er = lane >> 2, cg = lane & 3;
+  // EMIT: after emit_transpose lane l's rows are 32 m + er (phase of
+  // acc[0..1]) and 32 m + 16 + er (acc[2..3]), its blocks of a tile
+  // 4 cg + {0, 1, 2, 3, 16, 17, 18, 19}
+  const int er = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 1) & 1) + 2 * (lane & 1) + (lane >> 5);
+  const int cg = (lane >> 2) & 3;
   uint32_t ecnt0 = 0u, ecnt1 = 0u;
+
   auto store_counts = [&]() {
     const int64_t r0 = row0 + 32 * m + er, r1 = r0 + 16;
     if (r0 < a.rows) a.cnt[(r0 * a.splits + split) * 4 + cg] = static_cast<int32_t>(ecnt0);
@@ -617,10 +653,10 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       for (int ks = 0; ks < 8; ++ks) afrag[ms][ks] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ks);
     }
   }
-  if constexpr (EMIT)
-    if (tid < RG) sthr[tid] = a.thr[row0 + tid];
   // visible columns (wave 0, lane l: rows l and l + 64): blocks (p + 1) / 4,
   // of which every bstride-th is a column
+  if constexpr (EMIT)
+    if (tid < RG) sthr[tid] = a.thr[row0 + tid];
   if (wave == 0) {
     uint32_t mx = 0u, mn = 0x7FFFFFFFu;
 #pragma unroll
@@ -734,14 +770,10 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       EMIT ? a.cand + row0 * a.splits * 4 * a.cap : nullptr, static_cast<short>(0), RG * crow, 0x00020000);
   const int ebase = EMIT ? (32 * m + er) * crow + (split * 4 + cg) * a.cap * 8 : 0;
   const uint32_t capm1 = EMIT ? static_cast<uint32_t>(a.cap - 1) : 0u;
-  const uint32_t etile_w = lds_addr(etile) + 4 * (wave * 16 * kEPitch);
-  const uint32_t ewrite = etile_w + 4 * (h * kEPitch + r);        // lane (r, h) writes
-  const uint32_t eread = etile_w + 4 * (er * kEPitch + 8 * cg);   // lane l reads
   auto pair_emit = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast,
                        auto exact_c) {
     constexpr int m0 = decltype(m0c)::value;
-    // the phase's scores into the wave's tile: slot (ms, q4) of lane (r, h)
-    // is tile row 8 (ms - m0) + 2 q4 + h, column r
+    // slot s = 4 (ms - m0) + q4 of lane (r, h): phase row 2 s + h, block r
     float sc[8];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -749,42 +781,26 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       sc[4 + q4] = phase_score(x1, q4, exact_c);
     }
     if constexpr (!decltype(exact_c)::value) note_phase(sc);
-    lds_write_word<4 * 0 * kEPitch>(ewrite, __float_as_uint(sc[0]));
-    lds_write_word<4 * 2 * kEPitch>(ewrite, __float_as_uint(sc[1]));
-    lds_write_word<4 * 4 * kEPitch>(ewrite, __float_as_uint(sc[2]));
-    lds_write_word<4 * 6 * kEPitch>(ewrite, __float_as_uint(sc[3]));
-    lds_write_word<4 * 8 * kEPitch>(ewrite, __float_as_uint(sc[4]));
-    lds_write_word<4 * 10 * kEPitch>(ewrite, __float_as_uint(sc[5]));
-    lds_write_word<4 * 12 * kEPitch>(ewrite, __float_as_uint(sc[6]));
-    lds_write_word<4 * 14 * kEPitch>(ewrite, __float_as_uint(sc[7]));
-    // lane l: its row's threshold and visible blocks, and its 8 scores
-    const uint32_t prow = 32 * m + 8 * m0 + er;  // group row
-    uint32_t t, nv;
-    u32x4_t sums;
-    asm volatile(
-        "ds_read_b128 %0, %3\n\t"
-        "ds_read_b32 %1, %4\n\t"
-        "ds_read_b32 %2, %5\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=v"(sums), "=v"(t), "=v"(nv)
-        : "v"(eread), "v"(lds_addr(sthr) + 4 * prow), "v"(lds_addr(nvis) + 4 * prow)
-        : "memory");
-    u32x4_t sums2;
-    asm volatile("ds_read_b128 %0, %1 offset:16\n\ts_waitcnt lgkmcnt(0)" : "=v"(sums2) : "v"(eread) : "memory");
-    const uint32_t blk0 = static_cast<uint32_t>(nb0 + 8 * cg);
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __float_as_uint(sc[j]);
+    emit_transpose(v, lane);
+    const uint32_t t = static_cast<uint32_t>(lds_read_word(lds_addr(sthr) + 4 * (32 * m + 8 * m0 + er)));
+    const uint32_t blk0 = static_cast<uint32_t>(nb0 + 4 * cg);
     uint32_t& cnt = m0 == 0 ? ecnt0 : ecnt1;
     const int soff = m0 == 0 ? 0 : 16 * crow;
     // each path issues exactly 8 stores (the ring's vmcnt accounting)
     auto emit8 = [&](auto visc) {
+      uint32_t nv = 0u;
+      if constexpr (decltype(visc)::value) nv = static_cast<uint32_t>(lds_read_word(lds_addr(nvis) + 4 * (32 * m + 8 * m0 + er)));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t v = j < 4 ? sums[j] : sums2[j - 4];
-        const uint32_t blk = blk0 + j;
-        bool c = v >= t;
+        const uint32_t blk = blk0 + 16 * (j >> 2) + (j & 3);
+        bool c = v[j] >= t;
         if constexpr (decltype(visc)::value) c = c & live & (blk < nv);
         const uint32_t slot = cnt < capm1 ? cnt : capm1;  // past capacity: the row falls back
         const int voff = c ? ebase + 8 * static_cast<int>(slot) : kDrop;
-        __attribute__((ext_vector_type(2))) uint32_t e = {v, blk};
+        __attribute__((ext_vector_type(2))) uint32_t e = {v[j], blk};
         __builtin_amdgcn_raw_buffer_store_b64(e, crsrc, voff, soff, 0);
         cnt += c ? 1u : 0u;
       }
