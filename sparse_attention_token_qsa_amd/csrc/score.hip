@@ -537,11 +537,6 @@ __device__ __forceinline__ void lds_wait8(bf16x8_t (&b)[8]) {
                :
                : "memory");
 }
-// One LDS word written at addr + OFF, as inline assembly (no wait).
-template <int OFF>
-__device__ __forceinline__ void lds_write_word(uint32_t addr, uint32_t v) {
-  asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
-}
 // One LDS word read and its wait, as inline assembly.
 __device__ __forceinline__ int lds_read_word(uint32_t addr) {
   int v;
