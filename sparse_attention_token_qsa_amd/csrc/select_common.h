@@ -22,11 +22,15 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, int b) {
 }
 
 // The r-th largest (1 <= r <= 64) of the wave's 64 values, in every lane:
-// the largest x with at least r lanes holding a value >= x, built bit by bit.
+// the largest x with at least r lanes holding a value >= x, built bit by bit
+// from bit 31 down to bit LOW.  With LOW > 0 it is that value with its bits
+// below LOW cleared: still a value that at least r lanes reach, which is all
+// the prefilters need of it.
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t wave_rth_largest(uint32_t v, int r) {
   uint32_t x = 0u;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= LOW; --bit) {
     const uint32_t c = x | (1u << bit);
     if (__popcll(__ballot(v >= c)) >= r) x = c;
   }

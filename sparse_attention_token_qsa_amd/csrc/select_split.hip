@@ -159,7 +159,9 @@ __global__ __launch_bounds__(512) void select_chunk_kernel(const SplitArgs a) {
         t1 = max(t1, key[j]);
       }
       const int r = (keep + NW * TOPM - 1) / (NW * TOPM);
-      const uint32_t lw = wave_rth_largest(t2, r);
+      // the bound from the top 16 bits only: 16 fewer ballot steps in a
+      // latency-bound chain (16 rows over 256k: 18.7 -> 17.4 us)
+      const uint32_t lw = wave_rth_largest<16>(t2, r);
       const uint32_t wmax = wave_max_u32(t1);
       if (lane == 0) {
         red[wave] = lw;
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(1024) void select_merge_kernel(const SplitArgs a) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) t1 = max(t1, static_cast<uint32_t>(cv[j] >> 32));
   const int r = (keep + NW - 1) / NW;
-  const uint32_t lw = wave_rth_largest(t1, r);
+  const uint32_t lw = wave_rth_largest<16>(t1, r);  // top 16 bits, as in the chunk kernel
   const uint32_t wmax = wave_max_u32(t1);
   if (lane == 0) {
     red[wave] = lw;
