@@ -111,7 +111,7 @@ __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = g + 16 * k;
-    cs[k] = i < half ? rope_cos_sin_bf16x2(anchor, a.rp.inv_freq[i]) : 0u;
+    cs[k] = i < half ? rope_cos_sin_bf16x2(static_cast<int32_t>(anchor), a.rp.inv_freq[i]) : 0u;  // anchor < 2^31
   }
 
   // f32 mean of the 4 tokens in token order, cast to bf16.

@@ -169,9 +169,9 @@ __device__ __forceinline__ void cos_sin_small_angle(float angle, double& c, doub
 // the library cos/sin beyond: positions below 2^18 with frequencies at most
 // 1 keep |angle| < 2^18).  Both values are finite (|.| <= 1), so the
 // hardware round-to-nearest-even conversion is the bf16 rounding.
-__device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int64_t p, float f) {
+__device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int32_t p, float f) {
 #pragma clang fp contract(off)
-  const float angle = static_cast<float>(p) * f;
+  const float angle = static_cast<float>(p) * f;  // int32 -> f32 rounds as int64 -> f32 would
   float c = 0.0f, s = 0.0f;
   bool settled = false;
   if (fabsf(angle) < 262144.0f) {
