@@ -48,6 +48,11 @@ constexpr int kSampleStride = 16;
 constexpr int kCandMax = 2048;  // candidates one row's selector holds
 constexpr int kSampleTarget = 256;
 constexpr int kEmitTarget = 1024;
+// The fallback ring pass usually finds no flagged row group and its
+// workgroups exit at once; a quarter of the emit pass's workgroups makes
+// that idle launch ~2 us cheaper, and a flagged group is scored by 4
+// workgroups instead of 16.
+constexpr int kFallbackTarget = 256;
 
 int sample_rank(int keep_max) {
   const int r = (5 * keep_max + 2 * kSampleStride - 1) / (2 * kSampleStride);
@@ -446,7 +451,7 @@ hipError_t launch_score_select(const uint16_t* qhat, const int32_t* pos, int64_t
   f.score_cols = L.score_cols;
   f.status = nullptr;
   f.group_flag = gflag;
-  if ((e = launch_ring(f, kEmitTarget, stream)) != hipSuccess) return e;
+  if ((e = launch_ring(f, kFallbackTarget, stream)) != hipSuccess) return e;
   return launch_select_flagged(fscores, L.score_cols, pos, rows, tokens, keep_max, mask, status, rflag,
                                stream);
 }
