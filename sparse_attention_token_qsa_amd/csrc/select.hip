@@ -54,7 +54,6 @@ struct SelectArgs {
   int32_t* idx;        // index mode: [rows, idx_stride] kept token indices
   int64_t idx_stride;
   int32_t* counts;     // index mode: [rows] entries written
-  const int32_t* row_flag;  // non-null: only rows with a nonzero flag are selected
   int64_t xcd_groups;       // nonzero: rows are visited in group order (row_of)
 };
 
@@ -78,24 +77,39 @@ __device__ __forceinline__ int64_t row_of(const SelectArgs& a, int64_t b) {
 // (each kept block b as 4b .. 4b + 3, then the tail 4n .. p) go to
 // idx[r * idx_stride + i], i < counts[r] = 4 keep + tail, and -1 fills the
 // rest of the row's 4 keep_max + 3 entries; a refused row gets count 0.
-template <int NT, int KPT, int TOPM, bool VEC, bool IDX>
-__global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
-  constexpr int NW = NT / 64;
-  constexpr int kWords = IDX ? (KPT * NT + 31) / 32 : 1;  // bitmap of the row's blocks
+// The workgroup's LDS for one row, declared by each kernel that selects rows.
+template <int NT, int KPT, int TOPM, bool IDX>
+struct SelectLds {
+  static constexpr int NW = NT / 64;
+  static constexpr int kWords = IDX ? (KPT * NT + 31) / 32 : 1;  // bitmap of the row's blocks
   // The prefilter's per-wave rank r = ceil(512 / (NW * TOPM)) must stay <= 32.
-  constexpr bool kPrefilter = NW * TOPM >= 16;
-  constexpr int kCandCap = NT >= 1024 ? 4096 : 2048;
-  __shared__ __attribute__((aligned(16))) uint32_t hist[3 * 256];
-  __shared__ uint32_t red[2 * NW];
-  __shared__ uint64_t cand[kPrefilter ? kCandCap : 1];
-  __shared__ uint32_t ccount;  // candidates compacted (one LDS atomic per wave)
-  __shared__ uint32_t kbits[kWords];
+  static constexpr bool kPrefilter = NW * TOPM >= 16;
+  static constexpr int kCandCap = NT >= 1024 ? 4096 : 2048;
+  __attribute__((aligned(16))) uint32_t hist[3 * 256];
+  uint32_t red[2 * NW];
+  uint64_t cand[kPrefilter ? kCandCap : 1];
+  uint32_t ccount;  // candidates compacted (one LDS atomic per wave)
+  uint32_t kbits[kWords];
+};
+
+// The selection of row row_of(a, b) by the calling workgroup (every thread).
+template <int NT, int KPT, int TOPM, bool VEC, bool IDX>
+__device__ __forceinline__ void select_row(const SelectArgs& a, uint32_t b, SelectLds<NT, KPT, TOPM, IDX>& L) {
+  using LD = SelectLds<NT, KPT, TOPM, IDX>;
+  constexpr int NW = LD::NW;
+  constexpr int kWords = LD::kWords;
+  constexpr bool kPrefilter = LD::kPrefilter;
+  constexpr int kCandCap = LD::kCandCap;
+  uint32_t* hist = L.hist;
+  uint32_t* red = L.red;
+  uint64_t* cand = L.cand;
+  uint32_t& ccount = L.ccount;
+  uint32_t* kbits = L.kbits;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t row = row_of(a, blockIdx.x);
-  if (a.row_flag != nullptr && a.row_flag[row] == 0) return;  // uniform
+  const int64_t row = row_of(a, b);
   const int64_t T = a.tokens;
   uint8_t* mrow = a.mask + row * T;
   const int64_t p = a.pos[row];
@@ -384,12 +398,63 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
   }
 }
 
+template <int NT, int KPT, int TOPM, bool VEC, bool IDX>
+__global__ __launch_bounds__(NT) void select_kernel(const SelectArgs a) {
+  __shared__ SelectLds<NT, KPT, TOPM, IDX> L;
+  select_row<NT, KPT, TOPM, VEC, IDX>(a, blockIdx.x, L);
+}
+
+// Rows whose flag is nonzero only (the others left untouched), for a caller
+// that expects few of them: workgroup w owns rows [w per, w per + per), per
+// <= NT, reads their flags with one load per thread, lists the flagged ones
+// and selects them one after another.  With nothing flagged the launch costs
+// a flag load per row instead of a workgroup per row.
+template <int NT, int KPT, int TOPM, bool VEC>
+__global__ __launch_bounds__(NT) void select_flagged_kernel(const SelectArgs a, const int32_t* flag, int64_t rows,
+                                                             int per) {
+  __shared__ SelectLds<NT, KPT, TOPM, false> L;
+  __shared__ int32_t list[NT];
+  __shared__ uint32_t nlist;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t r = r0 + tid;
+  const bool mine = tid < per && r < rows && flag[r] != 0;
+  if (tid == 0) nlist = 0u;
+  __syncthreads();
+  const uint64_t bal = __ballot(mine);
+  uint32_t wbase = 0;
+  if (lane == 0 && bal != 0ull) wbase = atomicAdd(&nlist, static_cast<uint32_t>(__popcll(bal)));
+  wbase = read_lane(wbase, 0);
+  if (mine) list[wbase + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(tid);
+  __syncthreads();
+  const int n = static_cast<int>(nlist);
+  for (int k = 0; k < n; ++k) {
+    select_row<NT, KPT, TOPM, VEC, false>(a, static_cast<uint32_t>(r0 + list[k]), L);  // rows in index order
+    __syncthreads();  // this row's LDS read everywhere before the next row's
+  }
+}
+
+// LDS per CU on gfx950.  The prefill-batch select (512 threads, 32 keys per
+// thread) runs 3 workgroups per CU faster than 4 (172 against 206 us on the
+// 8192-row chunk over 64k; 2 per CU: 217 us), so its launch reserves enough
+// unused LDS that a fourth does not fit.
+constexpr size_t kLdsPerCu = 160 * 1024;
+template <int NT, int KPT, int TOPM, bool IDX>
+constexpr size_t select_lds_pad() {
+  if (!(NT == 512 && KPT == 32)) return 0;
+  constexpr size_t need = kLdsPerCu / 4 + 1024;  // per workgroup, so that 4 exceed the CU and 3 fit
+  constexpr size_t have = sizeof(SelectLds<NT, KPT, TOPM, IDX>);
+  return need > have ? need - have : 0;
+}
+
 template <int NT, int KPT, int TOPM, bool IDX>
 hipError_t launch_select_t(const SelectArgs& a, int64_t rows, bool vec, hipStream_t stream) {
+  constexpr size_t pad = select_lds_pad<NT, KPT, TOPM, IDX>();
+  static_assert(3 * (sizeof(SelectLds<NT, KPT, TOPM, IDX>) + pad) <= kLdsPerCu, "three workgroups fit a CU");
   if (vec)
-    select_kernel<NT, KPT, TOPM, true, IDX><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+    select_kernel<NT, KPT, TOPM, true, IDX><<<dim3(static_cast<unsigned>(rows)), dim3(NT), pad, stream>>>(a);
   else
-    select_kernel<NT, KPT, TOPM, false, IDX><<<dim3(static_cast<unsigned>(rows)), dim3(NT), 0, stream>>>(a);
+    select_kernel<NT, KPT, TOPM, false, IDX><<<dim3(static_cast<unsigned>(rows)), dim3(NT), pad, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -411,6 +476,41 @@ hipError_t launch_select_rows(const SelectArgs& args, int64_t rows, bool vec, hi
                        : launch_select_t<512, 32, 2, IDX>(a, rows, vec, stream);
   if (nmax <= 32768) return launch_select_t<1024, 32, 1, IDX>(a, rows, vec, stream);
   if (nmax <= 65536) return launch_select_t<1024, 64, 1, IDX>(a, rows, vec, stream);
+  return hipErrorInvalidValue;
+}
+
+// The geometries of launch_select_rows; at most 256 workgroups of `per`
+// rows each.
+template <int NT, int KPT, int TOPM>
+hipError_t launch_flagged_t(const SelectArgs& a, const int32_t* flag, int64_t rows, bool vec, hipStream_t stream) {
+  int64_t grid = rows < 256 ? rows : 256;
+  if (grid < 1) return hipSuccess;
+  int64_t per = (rows + grid - 1) / grid;
+  if (per > NT) {
+    per = NT;
+    grid = (rows + per - 1) / per;
+  }
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (vec)
+    select_flagged_kernel<NT, KPT, TOPM, true><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(
+        a, flag, rows, static_cast<int>(per));
+  else
+    select_flagged_kernel<NT, KPT, TOPM, false><<<dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream>>>(
+        a, flag, rows, static_cast<int>(per));
+  return hipGetLastError();
+}
+
+hipError_t launch_select_flagged_rows(const SelectArgs& a, const int32_t* flag, int64_t rows, bool vec,
+                                      hipStream_t stream) {
+  const int64_t nmax = a.tokens / kRatio;
+  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (nmax <= 1024) return launch_flagged_t<256, 4, 1>(a, flag, rows, vec, stream);
+  if (nmax <= 2048) return launch_flagged_t<256, 8, 1>(a, flag, rows, vec, stream);
+  if (nmax <= 4096) return launch_flagged_t<256, 16, 1>(a, flag, rows, vec, stream);
+  if (nmax <= 8192) return launch_flagged_t<512, 16, 2>(a, flag, rows, vec, stream);
+  if (nmax <= 16384) return launch_flagged_t<512, 32, 2>(a, flag, rows, vec, stream);
+  if (nmax <= 32768) return launch_flagged_t<1024, 32, 1>(a, flag, rows, vec, stream);
+  if (nmax <= 65536) return launch_flagged_t<1024, 64, 1>(a, flag, rows, vec, stream);
   return hipErrorInvalidValue;
 }
 
@@ -444,10 +544,10 @@ hipError_t launch_select_flagged(const float* scores, int64_t score_cols, const 
   a.keep_max = keep_max;
   a.mask = mask;
   a.status = status;
-  a.row_flag = row_flag;
+  a.xcd_groups = 0;  // the flagged kernel passes rows, not workgroup indices
   const bool vec = (score_cols % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0) &&
                    (tokens % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
-  return launch_select_rows<false>(a, rows, vec, stream);
+  return launch_select_flagged_rows(a, row_flag, rows, vec, stream);
 }
 
 hipError_t launch_select_indices(const float* scores, int64_t score_cols, const int32_t* pos,
