@@ -4,9 +4,9 @@
 namespace qsa {
 namespace {
 
-template <bool kVec>
+template <bool kVec, int kHalf>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const PoolArgs a) {
-  pool_group<kVec>(a, blockIdx.x);
+  pool_group<kVec, kHalf>(a, blockIdx.x);
 }
 
 }  // namespace
@@ -20,10 +20,17 @@ hipError_t launch_pool(const uint16_t* raw, int64_t key_stride, const uint16_t* 
   if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool vec = (key_stride % 8 == 0) && (reinterpret_cast<uintptr_t>(raw) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(pooled) % 16 == 0);
-  if (vec)
-    pool_kernel<true><<<dim3(static_cast<unsigned>(groups)), dim3(kPoolThreads), 0, stream>>>(a);
-  else
-    pool_kernel<false><<<dim3(static_cast<unsigned>(groups)), dim3(kPoolThreads), 0, stream>>>(a);
+  const dim3 grid(static_cast<unsigned>(groups)), block(kPoolThreads);
+  if (rp.rotary_dim == 64) {  // the pages' geometry, its pair count fixed at compile time
+    if (vec)
+      pool_kernel<true, 32><<<grid, block, 0, stream>>>(a);
+    else
+      pool_kernel<false, 32><<<grid, block, 0, stream>>>(a);
+  } else if (vec) {
+    pool_kernel<true, 0><<<grid, block, 0, stream>>>(a);
+  } else {
+    pool_kernel<false, 0><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -57,13 +57,20 @@ __device__ __forceinline__ uint32_t pool_nan_halves(uint32_t d) {
 }
 
 // The pooled keys of workgroup-sized group `group` (16 consecutive blocks).
-template <bool kVec>
+// kHalf: rotary_dim / 2 when fixed at compile time (the launch picks 32 for
+// rotary_dim 64), else 0 and taken from the arguments.
+template <bool kVec, int kHalf = 0>
 __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
   // one 128-channel bf16 row per block slot: the normed key, then (in place)
   // the rotated channels
   __shared__ __attribute__((aligned(16))) uint16_t ys[kPoolBlocksPerGroup][kHeadDim];
+  // (1 + w) in double for the 128 channels.  Every wave converts all of them,
+  // two per lane, and writes the same values, so a wave reads back only its
+  // own writes: a quarter of the conversions of eight per lane.
+  __shared__ __attribute__((aligned(16))) double wpt[kHeadDim];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int slot = tid >> 4;  // block slot within the group (16 lanes of one wave)
   const int g = tid & 15;     // channel group: channels 8g .. 8g+7
   const int64_t group_first = group * kPoolBlocksPerGroup;
@@ -74,13 +81,17 @@ __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
     first = complete > a.n_blocks ? complete - a.n_blocks : 0;
     count = complete - first;
   }
+  if (count <= 0) return;  // uniform: an empty window
   const bool live = blk < count;
   const int64_t b = first + blk;
 
-  // raw keys first: four 16-byte token rows per lane
+  // raw keys first: four 16-byte token rows per lane.  A lane past the range
+  // reads the range's last block instead (in bounds; its results are not
+  // stored), so every lane loads without a branch.
   uint4 v[4];
-  if (live) {
-    const uint16_t* base = a.raw + kRatio * b * a.key_stride + 8 * g;
+  {
+    const int64_t bl = live ? b : first + count - 1;
+    const uint16_t* base = a.raw + kRatio * bl * a.key_stride + 8 * g;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint16_t* src = base + t * a.key_stride;
@@ -93,26 +104,27 @@ __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
         v[t].w = src[6] | (static_cast<uint32_t>(src[7]) << 16);
       }
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = make_uint4(0u, 0u, 0u, 0u);
   }
-  double wp[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) wp[e] = 1.0 + static_cast<double>(bf16_to_f32(a.w[8 * g + e]));
+  {
+    wpt[2 * lane] = 1.0 + static_cast<double>(bf16_to_f32(a.w[2 * lane]));
+    wpt[2 * lane + 1] = 1.0 + static_cast<double>(bf16_to_f32(a.w[2 * lane + 1]));
+  }
 
   // cos/sin at the anchor 4b for the rotary pairs this lane rotates: pairs
   // i = g, g + 16, g + 32, g + 48 below rotary_dim / 2 (computed while the
   // loads are in flight)
-  const int rd = a.rp.rotary_dim;
-  const int half = rd >> 1;
+  const int half = kHalf > 0 ? kHalf : (a.rp.rotary_dim >> 1);
+  constexpr int kPairs = kHalf > 0 ? (kHalf + 15) / 16 : 4;  // pairs per lane, at most
+  // (with kHalf 32 the two pairs are the adjacent 2g and 2g + 1 instead)
   const int64_t anchor = kRatio * b;
-  uint32_t cs[4];
+  auto pair_of = [&](int k) { return kHalf == 32 ? 2 * g + k : g + 16 * k; };
+  float fr[kPairs];  // every frequency requested before the first evaluation
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = g + 16 * k;
-    cs[k] = i < half ? rope_cos_sin_bf16x2(static_cast<int32_t>(anchor), a.rp.inv_freq[i]) : 0u;  // anchor < 2^31
-  }
+  for (int k = 0; k < kPairs; ++k) fr[k] = a.rp.inv_freq[pair_of(k)];  // below 64
+  uint32_t cs[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k)
+    cs[k] = pair_of(k) < half ? rope_cos_sin_bf16x2(static_cast<int32_t>(anchor), fr[k]) : 0u;  // anchor < 2^31
 
   // f32 mean of the 4 tokens in token order, cast to bf16.
   float k0[8], k1[8], k2[8], k3[8], m[8];
@@ -121,12 +133,16 @@ __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
   unpack_bf16x8(v[2], k2);
   unpack_bf16x8(v[3], k3);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 8; e += 2) {
 #pragma clang fp contract(off)
-    float s = k0[e] + k1[e];
-    s = s + k2[e];
-    s = s + k3[e];
-    m[e] = rb_hw(s * 0.25f);
+    float s0 = k0[e] + k1[e], s1 = k0[e + 1] + k1[e + 1];
+    s0 = s0 + k2[e];
+    s1 = s1 + k2[e + 1];
+    s0 = s0 + k3[e];
+    s1 = s1 + k3[e + 1];
+    const uint32_t pk = cvt_pk_bf16(s0 * 0.25f, s1 * 0.25f);
+    m[e] = __uint_as_float(pk << 16);
+    m[e + 1] = __uint_as_float(pk & 0xFFFF0000u);
   }
 
   // (1 + w) RMSNorm in double, rounded to f32 and then to bf16.
@@ -134,11 +150,12 @@ __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += static_cast<double>(m[e]) * static_cast<double>(m[e]);
   const double r = inv_rms(row16_sum(ss), a.rp.eps);
+  wave_lds_sync();  // the weight table: this wave's own writes
   float y[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
 #pragma clang fp contract(off)
-    y[e] = rb_hw(static_cast<float>((static_cast<double>(m[e]) * r) * wp[e]));
+    y[e] = rb_hw(static_cast<float>((static_cast<double>(m[e]) * r) * wpt[8 * g + e]));
   }
   uint16_t* row = &ys[slot][0];
   *reinterpret_cast<uint4*>(row + 8 * g) =
@@ -149,25 +166,52 @@ __device__ __forceinline__ void pool_group(const PoolArgs& a, int64_t group) {
   // sum rounds to bf16, o_i = rb(rb(y_i c) - rb(y_{i+h} s)),
   // o_{i+h} = rb(rb(y_{i+h} c) + rb(y_i s)).  All of the row is read before
   // any rotated channel is written back in its place.
-  float x0[4], x1[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = g + 16 * k;
-    x0[k] = i < half ? bf16_to_f32(row[i]) : 0.0f;
-    x1[k] = i < half ? bf16_to_f32(row[i + half]) : 0.0f;
-  }
-  wave_lds_sync();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  if constexpr (kHalf == 32) {
+    // lane g rotates pairs 2g and 2g + 1: one 4-byte word of each half, and
+    // every conversion to bf16 takes two values
+    const uint32_t xa = *reinterpret_cast<const uint32_t*>(row + 2 * g);       // y_2g, y_2g+1
+    const uint32_t xb = *reinterpret_cast<const uint32_t*>(row + 2 * g + 32);  // y_2g+32, y_2g+33
+    wave_lds_sync();
+    {
 #pragma clang fp contract(off)
-    const int i = g + 16 * k;
-    if (i < half) {
-      const float c = __uint_as_float(cs[k] << 16);
-      const float sn = __uint_as_float(cs[k] & 0xFFFF0000u);
-      const float o0 = rb_hw(x0[k] * c) - rb_hw(x1[k] * sn);
-      const float o1 = rb_hw(x1[k] * c) + rb_hw(x0[k] * sn);
-      row[i] = static_cast<uint16_t>(pool_pack2(o0, 0.0f) & 0xFFFFu);
-      row[i + half] = static_cast<uint16_t>(pool_pack2(o1, 0.0f) & 0xFFFFu);
+    const float a0 = __uint_as_float(xa << 16), a1 = __uint_as_float(xa & 0xFFFF0000u);
+    const float b0 = __uint_as_float(xb << 16), b1 = __uint_as_float(xb & 0xFFFF0000u);
+    const float c0 = __uint_as_float(cs[0] << 16), s0 = __uint_as_float(cs[0] & 0xFFFF0000u);
+    const float c1 = __uint_as_float(cs[1] << 16), s1 = __uint_as_float(cs[1] & 0xFFFF0000u);
+    const uint32_t pac = cvt_pk_bf16(a0 * c0, a1 * c1);  // rb(y_i c)
+    const uint32_t pbs = cvt_pk_bf16(b0 * s0, b1 * s1);  // rb(y_{i+h} s)
+    const uint32_t pbc = cvt_pk_bf16(b0 * c0, b1 * c1);  // rb(y_{i+h} c)
+    const uint32_t pas = cvt_pk_bf16(a0 * s0, a1 * s1);  // rb(y_i s)
+    const uint32_t oa = cvt_pk_bf16(__uint_as_float(pac << 16) - __uint_as_float(pbs << 16),
+                                    __uint_as_float(pac & 0xFFFF0000u) - __uint_as_float(pbs & 0xFFFF0000u));
+    const uint32_t ob = cvt_pk_bf16(__uint_as_float(pbc << 16) + __uint_as_float(pas << 16),
+                                    __uint_as_float(pbc & 0xFFFF0000u) + __uint_as_float(pas & 0xFFFF0000u));
+    *reinterpret_cast<uint32_t*>(row + 2 * g) = oa;
+    *reinterpret_cast<uint32_t*>(row + 2 * g + 32) = ob;
+    }
+  } else {
+    float x0[kPairs], x1[kPairs];
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int i = g + 16 * k;
+      x0[k] = i < half ? bf16_to_f32(row[i]) : 0.0f;
+      x1[k] = i < half ? bf16_to_f32(row[i + half]) : 0.0f;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+#pragma clang fp contract(off)
+      const int i = g + 16 * k;
+      if (i < half) {
+        const float c = __uint_as_float(cs[k] << 16);
+        const float sn = __uint_as_float(cs[k] & 0xFFFF0000u);
+        const uint32_t pc = cvt_pk_bf16(x0[k] * c, x1[k] * c);    // rb(y_i c), rb(y_{i+h} c)
+        const uint32_t ps = cvt_pk_bf16(x1[k] * sn, x0[k] * sn);  // rb(y_{i+h} s), rb(y_i s)
+        const uint32_t o = cvt_pk_bf16(__uint_as_float(pc << 16) - __uint_as_float(ps << 16),
+                                       __uint_as_float(pc & 0xFFFF0000u) + __uint_as_float(ps & 0xFFFF0000u));
+        row[i] = static_cast<uint16_t>(o & 0xFFFFu);
+        row[i + half] = static_cast<uint16_t>(o >> 16);
+      }
     }
   }
   wave_lds_sync();

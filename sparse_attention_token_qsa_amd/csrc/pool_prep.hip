@@ -17,13 +17,13 @@ namespace {
 
 static_assert(kPoolThreads == kPrepThreads, "one workgroup size for both stages");
 
-template <bool kVec>
+template <bool kVec, int kHalf>
 __global__ __launch_bounds__(kPoolThreads) void pool_prep_kernel(const PoolArgs pa, const PrepArgs qa,
                                                                  const int64_t prep_groups) {
   if (static_cast<int64_t>(blockIdx.x) < prep_groups)  // uniform across the workgroup
     prep_group(qa, blockIdx.x);
   else
-    pool_group<kVec>(pa, static_cast<int64_t>(blockIdx.x) - prep_groups);
+    pool_group<kVec, kHalf>(pa, static_cast<int64_t>(blockIdx.x) - prep_groups);
 }
 
 }  // namespace
@@ -53,10 +53,17 @@ hipError_t launch_pool_prep(const uint16_t* raw, int64_t key_stride, const uint1
   if (grid == 0) return hipSuccess;
   const bool vec = (key_stride % 8 == 0) && (reinterpret_cast<uintptr_t>(raw) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(pooled) % 16 == 0);
-  if (vec)
-    pool_prep_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kPoolThreads), 0, stream>>>(pa, qa, prep_groups);
-  else
-    pool_prep_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kPoolThreads), 0, stream>>>(pa, qa, prep_groups);
+  const dim3 g(static_cast<unsigned>(grid)), block(kPoolThreads);
+  if (rp.rotary_dim == 64) {  // the pages' geometry, its pair count fixed at compile time
+    if (vec)
+      pool_prep_kernel<true, 32><<<g, block, 0, stream>>>(pa, qa, prep_groups);
+    else
+      pool_prep_kernel<false, 32><<<g, block, 0, stream>>>(pa, qa, prep_groups);
+  } else if (vec) {
+    pool_prep_kernel<true, 0><<<g, block, 0, stream>>>(pa, qa, prep_groups);
+  } else {
+    pool_prep_kernel<false, 0><<<g, block, 0, stream>>>(pa, qa, prep_groups);
+  }
   return hipGetLastError();
 }
 

@@ -89,6 +89,16 @@ __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to
 // non-NaN input; a NaN stays a NaN but keeps its sign and payload).
 __device__ __forceinline__ float rb_hw(float f) { return static_cast<float>(static_cast<__bf16>(f)); }
 
+// Two floats to packed bf16 (lo in bits 0..15) by the hardware conversion
+// (round to nearest even; a NaN keeps its sign and payload), as one
+// instruction: left to itself the compiler may split a packed conversion
+// whose halves are used apart into two.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+
 // Two floats to packed bf16 (lo in bits 0..15) by the hardware conversion,
 // with every NaN written as the canonical 0x7FC0.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -187,15 +197,11 @@ __device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int32_t p, float f) {
     c = static_cast<float>(cd);  // the f32 rounding first
     s = static_cast<float>(sd);
   }
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t v;
-  v[0] = static_cast<__bf16>(c);
-  v[1] = static_cast<__bf16>(s);
-  return __builtin_bit_cast(uint32_t, v);
+  return cvt_pk_bf16(c, s);
 }
 
 // Sum over the 16 lanes of a DPP row, returned in all 16 (rotations 8, 4, 2,
-// 1).  Used on the sums of squares of bf16 values behind the RMSNorm: each
+// 1; every lane's source lies in its own row, so no old value is needed).  Used on the sums of squares of bf16 values behind the RMSNorm: each
 // square has at most 16 significant bits, so a double sum of 128 of them is
 // exact, and the same in any order, while the vector's channel magnitudes
 // span less than about 2^18 (the smallest square's lowest bit then stays
@@ -206,8 +212,8 @@ __device__ __forceinline__ uint32_t rope_cos_sin_bf16x2(int32_t p, float f) {
 __device__ __forceinline__ double row16_sum(double v) {
 #define QSA_ROR_STEP(CTRL)                                                                  \
   {                                                                                         \
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false); \
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false); \
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);      \
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);      \
     v += __hiloint2double(hi, lo);                                                          \
   }
   QSA_ROR_STEP(0x128)  // row_ror 8
