@@ -21,7 +21,7 @@ template <bool kVec, int kHalf>
 __global__ __launch_bounds__(kPoolThreads) void pool_prep_kernel(const PoolArgs pa, const PrepArgs qa,
                                                                  const int64_t prep_groups) {
   if (static_cast<int64_t>(blockIdx.x) < prep_groups)  // uniform across the workgroup
-    prep_group(qa, blockIdx.x);
+    prep_group<kHalf>(qa, blockIdx.x);
   else
     pool_group<kVec, kHalf>(pa, static_cast<int64_t>(blockIdx.x) - prep_groups);
 }

@@ -4,7 +4,10 @@
 namespace qsa {
 namespace {
 
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) { prep_group(a, blockIdx.x); }
+template <int kHalf>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) {
+  prep_group<kHalf>(a, blockIdx.x);
+}
 
 }  // namespace
 
@@ -25,7 +28,11 @@ hipError_t launch_prep(const uint16_t* q, int64_t q_stride, const int32_t* pos, 
   a.rp = rp;
   const int64_t grid = (rows + kPrepRows - 1) / kPrepRows;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  prep_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), 0, stream>>>(a);
+  const dim3 g(static_cast<unsigned>(grid)), b(kPrepThreads);
+  if (rp.rotary_dim == 64)  // the pages' geometry, its pair count fixed at compile time
+    prep_kernel<32><<<g, b, 0, stream>>>(a);
+  else
+    prep_kernel<0><<<g, b, 0, stream>>>(a);
   return hipGetLastError();
 }
 
