@@ -588,8 +588,8 @@ def decode_next(d: Device, torch, qsa):
 
 def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko, vo, otab, gather_bytes):
     """One production decode step with the cache length in a device word:
-    pool the block the new token completed, prep, score, index-list select,
-    K/V gather.  Timed as eager launches and as one captured HIP graph
+    pool the block the new token completed and prep the queries (one
+    launch), score, index-list select, K/V gather.  Timed as eager launches and as one captured HIP graph
     replayed back to back (positions and cache fixed; each replay redoes the
     same step), and cold (caches flushed before each step, one event pair
     around it), with the step's algorithmic bytes: one pooled block, the
@@ -600,8 +600,7 @@ def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko,
     dt = torch.full((1,), d.T, dtype=torch.int32, device="cuda:0")
 
     def step():
-        qsa.qsa_pool_window(d.raw, d.wk, rd, th, eps, dt, 1, d.pooled, d.status)
-        qsa.qsa_prep_queries_dev(d.q, d.pos, d.wq, rd, th, eps, dt, d.T, d.qhat, d.status)
+        qsa.qsa_pool_prep_dev(d.raw, d.wk, d.q, d.pos, d.wq, rd, th, eps, dt, 1, d.pooled, d.qhat, d.status)
         qsa.qsa_score_prepped_dev(d.qhat, d.pos, d.pooled, dt, d.T, d.scores, d.cols, d.status)
         qsa.qsa_select_indices_dev(d.scores, d.cols, d.pos, dt, d.T, w["budget"], idx, counts, d.status, d.ws)
         qsa.qsa_gather_kv(kc, vc, table, 0, n_pages, idx, counts, ko, vo, otab, d.status)
@@ -625,7 +624,7 @@ def decode_graph(d: Device, torch, qsa, idx, counts, kc, vc, table, n_pages, ko,
     if qsa.check_status(d.status) != 0:
         raise RuntimeError("device status set in the captured decode step")
     del graph
-    return {"stages": "pool_window(1 block) + prep + score + select_indices + gather",
+    return {"stages": "pool_prep(1 block + queries) + score + select_indices + gather",
             "eager_us": eager_us, "graph_replay_us": replay_us, "cold_us": cold_us, "alg_bytes": alg,
             "hbm_frac_eager": round(alg / (eager_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "hbm_frac_cold": round(alg / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
