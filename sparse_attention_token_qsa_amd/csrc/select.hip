@@ -100,6 +100,12 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, uint32_t b, Sele
   constexpr int kWords = LD::kWords;
   constexpr bool kPrefilter = LD::kPrefilter;
   constexpr int kCandCap = LD::kCandCap;
+  // Few-row geometries (1024 threads per row: decode batches and single
+  // rows, latency-bound) take the leaner compaction and mask code below.  The
+  // prefill batch keeps the longer forms: its rows stream HBM at the memory
+  // system's limit, and the leaner code, with fewer instructions between the
+  // stores, measured slower there (compaction 172 -> 178-183 us, mask -> 201).
+  constexpr bool kLean = NT >= 1024;
   uint32_t* hist = L.hist;
   uint32_t* red = L.red;
   uint64_t* cand = L.cand;
@@ -244,16 +250,47 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, uint32_t b, Sele
       const uint32_t incl = wave_incl_sum(mine);
       uint32_t wbase = 0;
       if (lane == 63) wbase = atomicAdd(&ccount, incl);
-      uint32_t at = read_lane(wbase, 63) + incl - mine;
-      {
-        const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
+      if constexpr (kLean) {
+        wbase = read_lane(wbase, 63);
+        uint32_t at = wbase + incl - mine;
+        if (wbase + read_lane(incl, 63) <= static_cast<uint32_t>(kCandCap)) {  // uniform: the wave's slots fit
+          // composite low word ~b = ~b0 - (b - b0) from one base per thread;
+          // the slot's LDS address advances by 8 bytes per candidate
+          const uint32_t nb0 = opaque(~static_cast<uint32_t>(VEC ? 4 * tid : tid));
+          uint64_t* slot = cand + at;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-          const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
-          const uint32_t kk = opaque(key[j]);
-          if (kk >= L) {
-            if (at < static_cast<uint32_t>(kCandCap)) cand[at] = composite(kk, b);
-            ++at;
+          for (int j = 0; j < KPT; ++j) {
+            const uint32_t off = VEC ? 4 * (j >> 2) * NT + (j & 3) : j * NT;
+            const uint32_t kk = opaque(key[j]);
+            if (kk >= L) {
+              *slot = (static_cast<uint64_t>(kk) << 32) | (nb0 - off);
+              ++slot;
+            }
+          }
+        } else {
+          const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
+#pragma unroll
+          for (int j = 0; j < KPT; ++j) {
+            const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
+            const uint32_t kk = opaque(key[j]);
+            if (kk >= L) {
+              if (at < static_cast<uint32_t>(kCandCap)) cand[at] = composite(kk, b);
+              ++at;
+            }
+          }
+        }
+      } else {
+        uint32_t at = read_lane(wbase, 63) + incl - mine;
+        {
+          const int t = static_cast<int>(opaque(static_cast<uint32_t>(tid)));
+#pragma unroll
+          for (int j = 0; j < KPT; ++j) {
+            const int b = VEC ? 4 * (t + (j >> 2) * NT) + (j & 3) : t + j * NT;
+            const uint32_t kk = opaque(key[j]);
+            if (kk >= L) {
+              if (at < static_cast<uint32_t>(kCandCap)) cand[at] = composite(kk, b);
+              ++at;
+            }
           }
         }
       }
@@ -367,7 +404,42 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, uint32_t b, Sele
     if (tid == 0) a.counts[row] = 4 * keep + tail;
     return;
   }
-  if constexpr (VEC) {
+  if constexpr (VEC && kLean) {
+    // One test per block: C(b) >= max(C*, lowkey << 32) is kept() (when the
+    // search returned a bin floor below lowkey << 32, every candidate is
+    // kept, and the candidates are exactly the keys >= lowkey), and it is
+    // false for every slot past the prefix (key 0, while lowkey >= 1).  Past
+    // the prefix only block n is nonzero: the tail tokens.
+    const uint64_t cthr = cstar > (static_cast<uint64_t>(lowkey) << 32) ? cstar : static_cast<uint64_t>(lowkey) << 32;
+    const int tail = static_cast<int>(p + 1 - 4 * static_cast<int64_t>(n));  // 0..3
+    const uint32_t tailw = tail > 0 ? 0x01010101u >> (32 - 8 * tail) : 0u;
+    const int64_t qlim64 = (T + 15) >> 4;  // 16-byte mask chunks in the row
+    const int qlim = qlim64 < 0x7FFFFFFF ? static_cast<int>(qlim64) : 0x7FFFFFFF;
+    // The test in 32-bit words: key > K, or key == K and b <= ~(low word),
+    // K the high word (a 64-bit compare would pair every key register with a
+    // scratch register)
+    const uint32_t kthr = static_cast<uint32_t>(cthr >> 32);
+    const uint32_t bmax = ~static_cast<uint32_t>(cthr);
+#pragma unroll
+    for (int g = 0; g < KPT / 4; ++g) {
+      const int q = tid + g * NT;
+      if (q < qlim) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t kk = opaque(key[4 * g + i]);
+          const uint32_t b = static_cast<uint32_t>(4 * q + i);
+          wv[i] = (kk > kthr || (kk == kthr && b <= bmax)) ? 0x01010101u : 0u;
+        }
+        if (q == (n >> 2)) {  // the chunk holding block n: one lane of the row
+          asm volatile("");   // a branch, not selects in every chunk
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv[i] = i == (n & 3) ? tailw : wv[i];
+        }
+        store_stream(reinterpret_cast<uint4*>(mrow) + q, wv[0], wv[1], wv[2], wv[3]);
+      }
+    }
+  } else if constexpr (VEC) {
 #pragma unroll
     for (int g = 0; g < KPT / 4; ++g) {
       const int q = tid + g * NT;
