@@ -8,14 +8,15 @@
 // is owned by 16 lanes (of one wave) holding 8 channels each, so one block's
 // four 256-byte token rows are read as four 16-byte loads per lane and the
 // pooled 256-byte row leaves as one 16-byte store per lane.  The loads are
-// issued first; each lane's cos/sin (for the rotary pairs g, g + 16, ... it
-// rotates) overlap them.  The RMSNorm statistic is a 16-lane DPP reduction
-// in double.  The RoPE goes pair by pair through the block's row in LDS, so
-// every lane rotates (two pairs each at rotary_dim 64) and any even
-// rotary_dim works; a block's lanes share a wave, so wave-level ordering of
-// the LDS traffic suffices.  Roundings to bf16 use the hardware's
-// round-to-nearest-even conversion; a NaN result is written as 0x7FC0.  The
-// stage is HBM-bound: 1 KiB read and 256 B written per block.
+// issued first; each lane's cos/sin (for the rotary pairs it rotates: 2g and
+// 2g + 1 at rotary_dim 64, else g, g + 16, ... below rotary_dim / 2) overlap
+// them.  The RMSNorm statistic is a 16-lane DPP reduction in double.  The
+// RoPE goes pair by pair through the block's row in LDS, so every lane
+// rotates and any even rotary_dim works; a block's lanes share a wave, so
+// wave-level ordering of the LDS traffic suffices.  Roundings to bf16 use the
+// hardware's round-to-nearest-even conversion; a NaN result is written as
+// 0x7FC0.  The stage moves 1 KiB read and 256 B written per block; on long
+// caches its instruction issue, more than HBM, sets its time.
 #pragma once
 
 #include "qsa_device.h"
