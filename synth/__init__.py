@@ -115,6 +115,28 @@ def apply_dups(pooled: np.ndarray, dup_blocks) -> np.ndarray:
     return out
 
 
+def rope_sweep(rotary_dim: int, theta: float, tokens: int = 262147, rows: int = 8192, seed: int = 31) -> dict:
+    """Inputs for checking the rotary embedding over a whole cache: raw keys
+    N(0, 1) for `tokens` tokens (every 4-token block anchor up to the longest
+    cache the library accepts), `rows` N(0, 1) query rows at positions 0..15,
+    the last 16 positions and uniform ones between, norm weights N(0, 0.05).
+    The draws do not depend on rotary_dim or theta, which are only recorded."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    keys = rng.standard_normal((tokens, HEAD_DIM), dtype=np.float32)
+    qs = rng.standard_normal((rows, HEADS, HEAD_DIM), dtype=np.float32)
+    w_k = (rng.standard_normal(HEAD_DIM) * 0.05).astype(np.float32)
+    w_q = (rng.standard_normal(HEAD_DIM) * 0.05).astype(np.float32)
+    ends = np.concatenate([np.arange(16), np.arange(tokens - 16, tokens)])
+    pos = np.concatenate([ends, rng.integers(16, tokens - 16, size=rows - len(ends))])
+    return dict(
+        wid=0, name=f"rope-sweep-{tokens}", tokens=tokens, budget=2048,
+        rotary_dim=rotary_dim, theta=theta, eps=EPS,
+        raw_keys=bf16_bits(keys), queries=bf16_bits(qs),
+        k_norm_w=bf16_bits(w_k), q_norm_w=bf16_bits(w_q),
+        pos=np.ascontiguousarray(pos, dtype=np.int32), dup_blocks=np.zeros(0, dtype=np.int64),
+    )
+
+
 def single_row(wid: int, position: int) -> dict:
     """One query row (workload wid's first query) at `position` over that
     workload's key cache: the pages' one-row select shapes (64k, 256k)."""
