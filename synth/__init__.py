@@ -115,7 +115,7 @@ def apply_dups(pooled: np.ndarray, dup_blocks) -> np.ndarray:
     return out
 
 
-def rope_sweep(rotary_dim: int, theta: float, tokens: int = 262147, rows: int = 8192, seed: int = 31) -> dict:
+def rope_sweep(rotary_dim: int, theta: float, tokens: int = 262147, rows: int = 8190, seed: int = 31) -> dict:
     """Inputs for checking the rotary embedding over a whole cache: raw keys
     N(0, 1) for `tokens` tokens (every 4-token block anchor up to the longest
     cache the library accepts), `rows` N(0, 1) query rows at positions 0..15,

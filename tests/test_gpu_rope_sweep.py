@@ -6,7 +6,7 @@ and keep it only when its error bound cannot move the bf16 rounding, else in
 double; the CPU tests check that certificate on every f32 angle with the host
 build of the same code.  Here the device path itself meets the oracle at
 every block anchor 4b of a 262147-token cache (the longest accepted) and at
-8192 query positions spread over it, for rotary tables of the pages'
+8190 query positions spread over it (the last prep workgroup partly empty), for rotary tables of the pages'
 geometry (rotary_dim 64, the launch's fixed-pair kernel) and others (the
 general kernel): [SCORE] summary, keys roped at the block's first token and
 queries at the row's own position, with bf16 rounding after every rotary
