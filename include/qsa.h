@@ -16,7 +16,10 @@
  *     row-major, in device memory, owned by the caller.
  *   - The library allocates, frees, synchronises and reads back nothing.
  *     All work is enqueued on `stream` (a hipStream_t; NULL = null stream).
- *     Calls are thread-safe and keep no state between calls.
+ *     Calls are thread-safe and keep no state between calls, with one
+ *     exception: qsa_select_mask_noalloc works in a library-owned device
+ *     array per GPU, whose address it looks up once under a lock, and calls
+ *     of it that overlap on one GPU race (see there).
  *   - Host-side refusals return a negative QSA_ERR_* code before any launch;
  *     nothing is written then.  An empty launch (zero rows / tokens / blocks)
  *     returns QSA_OK and enqueues nothing.
