@@ -25,6 +25,18 @@ __device__ __forceinline__ int64_t live_tokens(int64_t ceiling, const int32_t* d
   return t < 0 ? 0 : ceiling;
 }
 
+// Row group of entry k of XCD x's share when G row groups (G % 8 == 0) are
+// dealt to the 8 XCDs, each share walked in ascending k.  On a causal batch a
+// row group's length grows linearly with its index, and the launch lasts as
+// long as the XCD with the most work: with G % 16 == 0 each pair of entries
+// takes group x and its mirror 15 - x of one 16-group band, so every share
+// (and every half of a share walked in turn) sums to the same length; else
+// the XCD takes every eighth group.  A bijection of [0, G).
+__device__ __forceinline__ int xcd_share_group(int x, int k, int G) {
+  if ((G & 15) == 0) return 16 * (k >> 1) + ((k & 1) ? 15 - x : x);
+  return x + 8 * k;
+}
+
 // score scale 1/sqrt(head dim), rounded once to f32
 constexpr float kScale = static_cast<float>(0.088388347648318440550);
 

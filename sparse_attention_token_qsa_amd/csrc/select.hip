@@ -59,18 +59,19 @@ struct SelectArgs {
 
 // Row of workgroup b.  Any order gives the same output; the order decides
 // which scores are still in the memory-side cache when they are read.  The
-// ring scorer (score.hip) gives each of the 8 XCDs one eighth of the 128-row
-// groups and walks its share in ascending order, so its last workgroups write
-// the top groups of every share.  For a batch of 1024 g rows (g groups per
-// share) the select visits the groups of local index g - 1 of all shares
-// first, then g - 2, and so on: workgroup b takes group k = b / 128 in that
-// order, row 128 ((k % 8) g + g - 1 - k / 8) + b % 128, a bijection on the
-// batch's rows.  Measured on the 8192-row prefill chunk over 64k: 173 against
-// 178 us in index order.
+// ring scorer (score.hip) deals the 128-row groups of a batch of 1024 g rows
+// to the 8 XCDs, g groups per share (xcd_share_group), and each XCD walks its
+// share in ascending entry order, so its last workgroups write the last
+// entries of every share.  The select visits entry g - 1 of all shares first,
+// then g - 2, and so on: workgroup b takes visit k = b / 128, the group of
+// entry g - 1 - k / 8 of share k % 8, and row b % 128 of it, a bijection on
+// the batch's rows.  Measured on the 8192-row prefill chunk over 64k: 173
+// against 178 us in index order.
 __device__ __forceinline__ int64_t row_of(const SelectArgs& a, int64_t b) {
   if (a.xcd_groups == 0) return b;
-  const int64_t k = b >> 7;
-  return (((k & 7) * a.xcd_groups + a.xcd_groups - 1 - (k >> 3)) << 7) + (b & 127);
+  const int k = static_cast<int>(b >> 7);
+  const int g = static_cast<int>(a.xcd_groups);
+  return (static_cast<int64_t>(xcd_share_group(k & 7, g - 1 - (k >> 3), 8 * g)) << 7) + (b & 127);
 }
 
 // IDX: instead of the mask, row r's kept token indices in ascending order
