@@ -739,6 +739,42 @@ def test_score_long_batches_ragged_rows_bad_positions_nan_key():
     assert worst <= SCORE_ATOL
 
 
+@pytest.mark.parametrize("R", [1152, 3072, 4096])
+def test_ring_scorer_row_group_shares(R):
+    """The ring scorer deals its 128-row groups to the 8 XCDs by group count:
+    9 groups (1152 rows) in contiguous eighths of the tasks, 24 groups (3072
+    rows) every eighth group, 32 groups (4096 rows) mirror pairs of 16-group
+    bands.  On causal rows over 4k tokens (positions from 0 to the last
+    token) every score equals the one-call scorer's bit for bit, columns past
+    each prefix keep their sentinel, and 64 sampled rows are within the bound
+    of the oracle."""
+    w = workload(2)
+    T = w["tokens"]
+    rng = np.random.default_rng(1000 + R)
+    pos = np.sort(rng.integers(0, T, size=R)).astype(np.int32)
+    pos[-1] = T - 1
+    q = w["queries"][rng.integers(0, len(w["pos"]), size=R)]
+    pooled = oracle_pooled(2)
+    cols = T // 4
+    sentinel = np.float32(-7.25)
+    note(f"ring shares: {R} rows ({-(-R // 128)} groups) over {T} tokens")
+    got, st = gpu_scores_prepped(w, u16_dev(pooled), pos=pos, q=q, score_cols=cols, sentinel=sentinel)
+    ref, st2 = gpu_scores(w, u16_dev(pooled), pos=pos, q=q, score_cols=cols, sentinel=sentinel)
+    assert st == 0 and st2 == 0
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    n = (pos.astype(np.int64) + 1) // 4
+    assert np.all(got[np.arange(cols)[None, :] >= n[:, None]] == sentinel)
+    rows = rng.choice(R, size=64, replace=False)
+    qhat = O.prep_queries(q[rows], pos[rows], w["q_norm_w"], w["rotary_dim"], w["theta"], w["eps"])
+    want = O.score_rows(qhat, pos[rows], pooled, T)
+    worst = 0.0
+    for i, r in enumerate(rows):
+        if len(want[i]):
+            worst = max(worst, float(np.max(np.abs(got[r, : len(want[i])].astype(np.float64) - want[i]))))
+    note(f"  max |gpu - oracle| over 64 rows = {worst:.3e}")
+    assert worst <= SCORE_ATOL
+
+
 def test_score_full_prefill_chunk_ring_equals_one_call_scorer():
     """Every score of the 8192-row prefill chunk over 64k (125.8 M pairs, the
     benchmarked launch: the 128-row ring scorer, one step loop over 32-block
