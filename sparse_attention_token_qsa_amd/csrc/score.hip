@@ -742,10 +742,16 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   // the lanes that produced a non-finite one; exact pass: score_exact (see
   // the end).
   uint64_t seen = 0u;
-  auto store_off = [&](int ms, int q4, int nb0, bool live, bool fast) {
-    if (fast) return vbase;
-    const int nv = lds_read_word(nvis_lane + 4 * (8 * ms + 2 * q4));
-    return (live && nb0 + col < nv) ? vbase : kDrop;
+  // fast_c: every column of the tile is visible to every row of the group
+  // (a compile-time choice, so the fast form is straight-line code; a
+  // run-time flag left a branch and exec-mask bookkeeping around each store)
+  auto store_off = [&](int ms, int q4, int nb0, bool live, auto fast_c) {
+    if constexpr (decltype(fast_c)::value) {
+      return vbase;
+    } else {
+      const int nv = lds_read_word(nvis_lane + 4 * (8 * ms + 2 * q4));
+      return (live && nb0 + col < nv) ? vbase : kDrop;
+    }
   };
   auto phase_score = [&](const f32x16_t& x, int q4, auto exact_c) {
     if constexpr (decltype(exact_c)::value)
@@ -761,7 +767,7 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
     t = max(t, __float_as_uint(sc[7]));
     seen |= __builtin_amdgcn_ballot_w64(t >= 0x7F800000u);
   };
-  auto pair_store = [&](const f32x16_t& x0, const f32x16_t& x1, int m0, int nb0, bool live, bool fast,
+  auto pair_store = [&](const f32x16_t& x0, const f32x16_t& x1, int m0, int nb0, bool live, auto fast,
                         auto exact_c) {
     float sc[8];
 #pragma unroll
@@ -822,10 +828,14 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
   };
   auto epilogue = [&](const f32x16_t& x0, const f32x16_t& x1, auto m0c, int nb0, bool live, bool fast,
                       auto exact_c) {
-    if constexpr (EMIT)
+    if constexpr (EMIT) {
       pair_emit(x0, x1, m0c, nb0, live, fast, exact_c);
-    else
-      pair_store(x0, x1, decltype(m0c)::value, nb0, live, fast, exact_c);
+    } else {
+      if (fast)
+        pair_store(x0, x1, decltype(m0c)::value, nb0, live, std::true_type{}, exact_c);
+      else
+        pair_store(x0, x1, decltype(m0c)::value, nb0, live, std::false_type{}, exact_c);
+    }
   };
 
 #pragma unroll
