@@ -482,9 +482,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_mfma_kernel(const ScoreAr
 // loads: a wave's loads and score stores retire in issue order, and the
 // stores issued since that tile's loads are counted (at most 63).
 //
-// Epilogue: phase A runs acc[0..1]'s MFMAs and stores the previous step's
-// acc[2..3] scores; phase B runs acc[2..3]'s MFMAs and stores acc[0..1]'s,
-// so relu / head sum / scale of one pair overlaps the other pair's MFMAs.
+// Epilogue: phase A stores the previous step's acc[2..3] scores before
+// acc[0..1]'s MFMAs; phase B stores acc[0..1]'s, threaded between
+// acc[2..3]'s MFMAs on interior tiles, so relu / head sum / scale of one
+// pair overlaps the other pair's MFMAs.
 // ---------------------------------------------------------------------------
 
 template <int WM>
@@ -879,12 +880,33 @@ __global__ __launch_bounds__(256, 2) void score_ring_kernel(const RingArgs a) {
       acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[1][ks], bf[ks], ks ? acc[1] : f32x16_t{}, 0, 0, 0);
     }
     // phase B: this step's acc[0..1]
+    // Interior tile: acc[0..1]'s score math and stores are threaded between
+    // acc[2..3]'s MFMAs (one MFMA, six VALU, a store every second MFMA), so a
+    // wave issues its own epilogue while its matrix pipe is busy; left to
+    // itself the compiler issued all 32 MFMAs first.  8192 prefill rows over
+    // 64k: 133.8 -> 128.1 and 129.0 -> 123.9 us in one-process A/Bs on two
+    // boxes, scores bit-identical.
+    if (!EMIT && nb0 + TILE <= nmin) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) {
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
+      }
+      pair_store(acc[0], acc[1], 0, nb0, true, std::true_type{}, std::false_type{});
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);  // a store every second MFMA
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[2][ks], bf[ks], ks ? acc[2] : f32x16_t{}, 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[3][ks], bf[ks], ks ? acc[3] : f32x16_t{}, 0, 0, 0);
+      }
+      epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin, std::false_type{});
     }
-    epilogue(acc[0], acc[1], std::integral_constant<int, 0>{}, nb0, true, nb0 + TILE <= nmin, std::false_type{});
     // Tile t + 1 has landed once at most N of this wave's memory operations
     // are outstanding, N = what was issued after its loads: the loads of
     // (D - 2) tiles and the stores of each step since (D - 1 steps in the
